@@ -1,0 +1,80 @@
+"""The CPU oracle against its pins (no GPU)."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import pins
+
+
+@pytest.fixture(scope="module", params=["c", "numpy"])
+def rec(request):
+    return oracle.recurrence_c if request.param == "c" else oracle.recurrence_numpy
+
+
+def test_golden_scan_orders():
+    pins.check_golden_scan(oracle.scan_order)
+
+
+def test_scan_order_closed_form():
+    pins.check_scan_closed_form(oracle.scan_order,
+                                [(1, 1), (1, 7), (7, 1), (5, 7), (8, 8), (40, 40), (80, 80), (13, 3)])
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 50), st.integers(1, 50))
+def test_scan_order_closed_form_random(gh, gw):
+    pins.check_scan_closed_form(oracle.scan_order, [(gh, gw)])
+
+
+@pytest.mark.parametrize("check", pins.ALL_REC_CHECKS, ids=lambda f: f.__name__)
+def test_recurrence_pins(rec, check):
+    check(rec)
+
+
+def test_golden_forward_all_directions(rec):
+    pins.check_golden_forward(oracle.scan_order, rec)
+
+
+def test_direction_invariants(rec):
+    pins.check_direction_invariants(oracle.scan_order, rec)
+
+
+def test_c_matches_numpy_twin():
+    rng = np.random.default_rng(11)
+    q, k, v, g = pins.rand_inputs(rng, 2, 200, 3, 16, 8, gate_scale=0.05)
+    a = oracle.recurrence_c(q, k, v, g)
+    b = oracle.recurrence_numpy(q, k, v, g)
+    assert np.max(np.abs(a - b)) / np.max(np.abs(b)) <= 1e-12
+
+
+def test_chunked_model_matches_recurrence():
+    pins.check_chunk_independence(oracle.recurrence_c, oracle.chunkwise)
+
+
+def test_chunked_model_states():
+    """S entering chunk n equals the recurrence state after token n*C-1."""
+    rng = np.random.default_rng(12)
+    q, k, v, g = pins.rand_inputs(rng, 1, 50, 1, 3, 2)
+    C = 16
+    _, U, a, S_in = oracle.chunkwise(q, k, v, g, C, return_states=True)
+    S = np.zeros((3, 2))
+    for t in range(50):
+        if t % C == 0:
+            np.testing.assert_allclose(S_in[0, 0, t // C], S, rtol=1e-12, atol=1e-12)
+        S = np.exp(g[0, t, 0])[:, None] * S + np.outer(k[0, t, 0], v[0, t, 0])
+    # a_n is the product of the chunk's per-token decays
+    for n in range(4):
+        np.testing.assert_allclose(a[0, 0, n], np.prod(np.exp(g[0, n * C:(n + 1) * C, 0]), axis=0),
+                                   rtol=1e-12)
+
+
+def test_forward_upcasts_exactly_and_matches_workload_shapes():
+    from recurrent_vision_token_gla_amd import workloads as W
+    w = W.WORKLOADS[0]
+    q, k, v, g = W.workload_inputs(w, 0)
+    assert q.dtype == np.float32 and q.shape == (1, 64, 1, 32)
+    o = oracle.gla_forward(q, k, v, g, w.grid_h, w.grid_w, w.directions(0))
+    o2 = oracle.gla_forward(q, k, v, g, w.grid_h, w.grid_w, w.directions(0), impl="numpy")
+    assert np.max(np.abs(o - o2)) <= 1e-12 * np.max(np.abs(o2))
+    assert np.all(g <= 0)
