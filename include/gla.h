@@ -1,0 +1,148 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) chunkwise forward of GTR's key-only
+ * gated linear attention.
+ *
+ * What is computed (GTR project page, "How GTR Works" and "A Kernel That
+ * Makes Recurrence Fast"; ai.info summary of GTR, "Methodology in Plain
+ * English"): for every batch element b and head h, the tokens of a
+ * grid_h x grid_w patch grid are visited in one of four scan orders; along
+ * that order a state S in R^{dk x dv} starts at zero and evolves as
+ *
+ *     S_t = diag(exp(gk_t)) S_{t-1} + k_t^T v_t,      o_t = q_t S_t,
+ *
+ * i.e. only the key-side dimensions decay (value-side decay fixed at one);
+ * the output is written back at each token's own grid position. gk is the
+ * log of the per-key-dimension decay (gk <= 0 is the contract; gk > 0 makes
+ * the state grow and may overflow). No query scaling is applied.
+ *
+ * How it is computed: the "same state update, different execution schedule"
+ * of the project page's kernel section. Tokens are cut into chunks of
+ * `chunk` tokens. Three kernels run back to back on the caller's stream:
+ *   1. chunk summaries   -- for every (chunk, head) in parallel: the chunk's
+ *                           total decay a_n and its state contribution U_n;
+ *   2. boundary scan     -- S_{n+1} = diag(a_n) S_n + U_n along the chunks;
+ *   3. chunk outputs     -- for every (chunk, head) in parallel: the causal
+ *                           intra-chunk decayed score tile (held in LDS)
+ *                           times V, plus the readout of S_n.
+ *
+ * Memory layout (all tensors caller-owned device memory, contiguous,
+ * row-major, raster token order):
+ *   q, k, gk : [B][T][H][dk]      v, o : [B][T][H][dv]      T = grid_h*grid_w
+ * dtype GLA_F16: q, k, v, gk, o are IEEE half. GLA_F32: they are float; q, k
+ * and v are rounded to half for the matrix-core products, gk stays float.
+ * Accumulation is float in both cases. Supported: dk, dv in {32, 64},
+ * chunk in {16, 32, 64}. Device pointers must be 16-byte aligned; the
+ * workspace 256-byte aligned.
+ *
+ * Directions: `dir` is a HOST array of B codes (GLA_L2R..GLA_B2T), one per
+ * batch element; pass B copies for a single direction. Left->right is the
+ * raster order; top->bottom walks the columns left to right, each column top
+ * to bottom; right->left and bottom->top are the full reversals of those.
+ *
+ * Execution: asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ * is the default stream). No call allocates, synchronises or reads device
+ * memory on the host, so every call can be captured in a HIP graph. Calls
+ * are stateless and may run concurrently on different workspaces. The
+ * library keeps no pointer after a call returns.
+ *
+ * Errors: arguments are checked on the host before any HIP call; a failing
+ * check returns a negative status and touches nothing. A failed launch
+ * returns GLA_E_HIP. Device faults surface at the caller's next
+ * synchronisation. Values are not checked: NaN and Inf propagate.
+ * Empty problems (B, H, grid_h or grid_w equal to 0) return GLA_OK and launch
+ * nothing; pointers are then not examined.
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { GLA_L2R = 0, GLA_R2L = 1, GLA_T2B = 2, GLA_B2T = 3 };
+enum { GLA_F16 = 0, GLA_F32 = 1 };
+enum {
+  GLA_OK = 0,
+  GLA_E_ARG = -1,          /* null/misaligned pointer, negative size, bad code */
+  GLA_E_UNSUPPORTED = -2,  /* dk, dv or chunk outside the supported set */
+  GLA_E_WORKSPACE = -3,    /* workspace smaller than gla_fwd_workspace_bytes */
+  GLA_E_HIP = -4           /* a HIP launch failed; see gla_last_error_detail */
+};
+
+/* Library ABI version (incremented on any signature or layout change). */
+int gla_abi_version(void);
+
+/* Bytes of workspace gla_fwd needs for this problem (0 for an empty one, or
+ * if the shape is unsupported or negative). */
+size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk,
+                               int dv, int chunk);
+
+/* Byte offsets, within the workspace, of the three intermediate arrays, so
+ * that callers (tests) can inspect them after the phase calls below:
+ *   U : float [B][H][N][dv][dk]   chunk summaries, stored transposed (row e)
+ *   a : float [B][H][N][dk]       per-chunk total decay exp(sum of gk)
+ *   S : half  [B][H][N][dv][dk]   state entering each chunk, transposed
+ * with N = ceil(T / chunk). Returns GLA_OK or GLA_E_ARG/GLA_E_UNSUPPORTED. */
+int gla_workspace_layout(int B, int H, int grid_h, int grid_w, int dk, int dv,
+                         int chunk, size_t* off_U, size_t* off_a,
+                         size_t* off_S, size_t* total_bytes);
+
+/* The whole forward: o = GLA(q, k, v, gk) along dir[b] for each batch
+ * element b (GTR project page, "A Kernel That Makes Recurrence Fast").
+ * Enqueues the three phases below. o must not be the same buffer as any
+ * input. */
+int gla_fwd(const void* q, const void* k, const void* v, const void* gk,
+            void* o, int B, int H, int grid_h, int grid_w, int dk, int dv,
+            const int32_t* dir, int chunk, int dtype, void* workspace,
+            size_t workspace_bytes, void* stream);
+
+/* Phase 1 alone: chunk summaries into the workspace's U and a (for every
+ * (chunk, head) in parallel; ai.info summary of GTR, "Methodology in Plain
+ * English"). U_n = sum_j diag(exp(B_n - b_j)) k_j^T v_j with b_j the
+ * in-chunk inclusive cumulative log-decay and B_n its last value;
+ * a_n = exp(B_n). */
+int gla_chunk_summaries(const void* k, const void* v, const void* gk, int B,
+                        int H, int grid_h, int grid_w, int dk, int dv,
+                        const int32_t* dir, int chunk, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Phase 2 alone: boundary-state scan over the chunk axis, S_0 = 0,
+ * S_{n+1} = diag(a_n) S_n + U_n, from the workspace's U and a into its S
+ * (project page, "A Kernel That Makes Recurrence Fast": only the boundary
+ * states are carried sequentially). */
+int gla_state_scan(int B, int H, int grid_h, int grid_w, int dk, int dv,
+                   int chunk, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Phase 3 alone: every chunk's outputs from its tokens and the workspace's
+ * S: o_i = sum_{j<=i} A_ij v_j + (q_i * exp(b_i)) S_n with
+ * A_ij = sum_d q_i[d] k_j[d] exp(b_i[d] - b_j[d]) (project page, "A Kernel
+ * That Makes Recurrence Fast": the output kernel fuses the within-chunk
+ * score-value product with the boundary-state readout). */
+int gla_chunk_outputs(const void* q, const void* k, const void* v,
+                      const void* gk, void* o, int B, int H, int grid_h,
+                      int grid_w, int dk, int dv, const int32_t* dir,
+                      int chunk, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Writes perm[t] = raster index of the token at scan position t, for
+ * t = 0 .. grid_h*grid_w-1, with the same device index arithmetic the loads
+ * and stores use (project page, "How GTR Works": four scan orders).
+ * perm_dev is device memory of grid_h*grid_w int32. */
+int gla_scan_perm(int32_t* perm_dev, int grid_h, int grid_w, int dir,
+                  void* stream);
+
+/* Static text for a status code; never NULL. */
+const char* gla_status_string(int status);
+
+/* Detail of the last GLA_E_HIP on the calling thread ("" if none). */
+const char* gla_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

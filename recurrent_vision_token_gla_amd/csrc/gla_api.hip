@@ -1,0 +1,217 @@
+// C ABI of the chunkwise key-only GLA forward (declared in include/gla.h).
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// then enqueues kernels on the caller's stream. Nothing here allocates,
+// synchronises or reads device memory, so the calls are graph-capturable.
+#include <stdio.h>
+#include <string.h>
+
+#include "gla.h"
+#include "gla_launch.h"
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+int fail_hip(hipError_t e, const char* where) {
+  snprintf(g_detail, sizeof(g_detail), "%s: %s", where, hipGetErrorString(e));
+  return GLA_E_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape check shared by every entry point. Returns GLA_OK and fills `p`, or
+// an error status. `empty` is set when there is nothing to compute.
+int make_problem(int B, int H, int gh, int gw, int dk, int dv, int chunk, int dtype,
+                 gla::Problem* p, bool* empty) {
+  if (B < 0 || H < 0 || gh < 0 || gw < 0) return GLA_E_ARG;
+  if (dtype != GLA_F16 && dtype != GLA_F32) return GLA_E_ARG;
+  if ((dk != 32 && dk != 64) || (dv != 32 && dv != 64)) return GLA_E_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GLA_E_UNSUPPORTED;
+  const long long T = (long long)gh * gw;
+  // element offsets are formed in 64-bit; T and the grid counts must fit int
+  if (T > 0x7fffffffLL || (long long)B * T * H > (1LL << 40)) return GLA_E_UNSUPPORTED;
+  *empty = (B == 0 || H == 0 || T == 0);
+  p->B = B; p->H = H; p->gh = gh; p->gw = gw; p->T = (int)T;
+  p->dk = dk; p->dv = dv; p->chunk = chunk; p->dtype = dtype;
+  p->N = (int)((T + chunk - 1) / chunk);
+  if (!*empty && (p->N > 0x7fffffff / 1 || H > 65535)) return GLA_E_UNSUPPORTED;
+  return GLA_OK;
+}
+
+int check_dirs(const int32_t* dir, int B) {
+  if (!dir) return GLA_E_ARG;
+  for (int b = 0; b < B; ++b)
+    if (dir[b] < GLA_L2R || dir[b] > GLA_B2T) return GLA_E_ARG;
+  return GLA_OK;
+}
+
+gla::DirPack pack_dirs(const int32_t* dir, int b0, int nb) {
+  gla::DirPack d;
+  memset(&d, 0, sizeof(d));
+  for (int i = 0; i < nb; ++i) d.w[i >> 4] |= (uint32_t)(dir[b0 + i] & 3) << (2 * (i & 15));
+  return d;
+}
+
+int check_ws(const gla::Problem& p, const void* ws, size_t ws_bytes) {
+  const gla::WsLayout w = gla::workspace_layout(p);
+  if (!ws) return GLA_E_ARG;
+  if (!aligned(ws, 256)) return GLA_E_ARG;
+  if (ws_bytes < w.total) return GLA_E_WORKSPACE;
+  return GLA_OK;
+}
+
+int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_ARG; }
+
+#define GLA_TRY(expr)            \
+  do {                           \
+    const int rc_ = (expr);      \
+    if (rc_ != GLA_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int gla_abi_version(void) { return 1; }
+
+size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv,
+                               int chunk) {
+  gla::Problem p;
+  bool empty;
+  if (make_problem(B, H, grid_h, grid_w, dk, dv, chunk, GLA_F16, &p, &empty) != GLA_OK)
+    return 0;
+  if (empty) return 0;
+  return gla::workspace_layout(p).total;
+}
+
+int gla_workspace_layout(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
+                         size_t* off_U, size_t* off_a, size_t* off_S, size_t* total_bytes) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, GLA_F16, &p, &empty));
+  if (!off_U || !off_a || !off_S || !total_bytes) return GLA_E_ARG;
+  const gla::WsLayout w = gla::workspace_layout(p);
+  *off_U = w.off_U;
+  *off_a = w.off_a;
+  *off_S = w.off_S;
+  *total_bytes = empty ? 0 : w.total;
+  return GLA_OK;
+}
+
+int gla_chunk_summaries(const void* k, const void* v, const void* gk, int B, int H,
+                        int grid_h, int grid_w, int dk, int dv, const int32_t* dir,
+                        int chunk, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
+  if (empty) return GLA_OK;
+  GLA_TRY(check_tensor(k));
+  GLA_TRY(check_tensor(v));
+  GLA_TRY(check_tensor(gk));
+  GLA_TRY(check_dirs(dir, B));
+  GLA_TRY(check_ws(p, workspace, workspace_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
+    const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
+    const hipError_t e = gla::launch_summaries(p, b0, nb, pack_dirs(dir, b0, nb), k, v, gk,
+                                               static_cast<char*>(workspace), s);
+    if (e != hipSuccess) return fail_hip(e, "chunk summaries launch");
+  }
+  return GLA_OK;
+}
+
+int gla_state_scan(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, GLA_F16, &p, &empty));
+  if (empty) return GLA_OK;
+  GLA_TRY(check_ws(p, workspace, workspace_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
+    const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
+    const hipError_t e = gla::launch_scan(p, b0, nb, static_cast<char*>(workspace), s);
+    if (e != hipSuccess) return fail_hip(e, "boundary scan launch");
+  }
+  return GLA_OK;
+}
+
+int gla_chunk_outputs(const void* q, const void* k, const void* v, const void* gk, void* o,
+                      int B, int H, int grid_h, int grid_w, int dk, int dv,
+                      const int32_t* dir, int chunk, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
+  if (empty) return GLA_OK;
+  GLA_TRY(check_tensor(q));
+  GLA_TRY(check_tensor(k));
+  GLA_TRY(check_tensor(v));
+  GLA_TRY(check_tensor(gk));
+  GLA_TRY(check_tensor(o));
+  if (o == q || o == k || o == v || o == gk) return GLA_E_ARG;
+  GLA_TRY(check_dirs(dir, B));
+  GLA_TRY(check_ws(p, workspace, workspace_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
+    const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
+    const hipError_t e = gla::launch_outputs(p, b0, nb, pack_dirs(dir, b0, nb), q, k, v, gk,
+                                             o, static_cast<const char*>(workspace), s);
+    if (e != hipSuccess) return fail_hip(e, "chunk outputs launch");
+  }
+  return GLA_OK;
+}
+
+int gla_fwd(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
+            int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
+  if (empty) return GLA_OK;
+  // validate everything before the first launch so that a bad call enqueues nothing
+  GLA_TRY(check_tensor(q));
+  GLA_TRY(check_tensor(k));
+  GLA_TRY(check_tensor(v));
+  GLA_TRY(check_tensor(gk));
+  GLA_TRY(check_tensor(o));
+  if (o == q || o == k || o == v || o == gk) return GLA_E_ARG;
+  GLA_TRY(check_dirs(dir, B));
+  GLA_TRY(check_ws(p, workspace, workspace_bytes));
+  GLA_TRY(gla_chunk_summaries(k, v, gk, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
+                              workspace, workspace_bytes, stream));
+  GLA_TRY(gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace, workspace_bytes,
+                         stream));
+  return gla_chunk_outputs(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
+                           workspace, workspace_bytes, stream);
+}
+
+int gla_scan_perm(int32_t* perm_dev, int grid_h, int grid_w, int dir, void* stream) {
+  if (grid_h < 0 || grid_w < 0) return GLA_E_ARG;
+  if (dir < GLA_L2R || dir > GLA_B2T) return GLA_E_ARG;
+  const long long T = (long long)grid_h * grid_w;
+  if (T == 0) return GLA_OK;
+  if (T > 0x7fffffffLL) return GLA_E_UNSUPPORTED;
+  if (!perm_dev || !aligned(perm_dev, 4)) return GLA_E_ARG;
+  const hipError_t e =
+      gla::launch_scan_perm(perm_dev, grid_h, grid_w, dir, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "scan perm launch");
+  return GLA_OK;
+}
+
+const char* gla_status_string(int status) {
+  switch (status) {
+    case GLA_OK: return "GLA_OK";
+    case GLA_E_ARG: return "GLA_E_ARG: invalid argument (null/misaligned pointer, negative size, bad code, aliasing)";
+    case GLA_E_UNSUPPORTED: return "GLA_E_UNSUPPORTED: dk, dv or chunk outside the supported set, or problem too large";
+    case GLA_E_WORKSPACE: return "GLA_E_WORKSPACE: workspace smaller than gla_fwd_workspace_bytes()";
+    case GLA_E_HIP: return "GLA_E_HIP: a HIP launch failed (see gla_last_error_detail)";
+    default: return "unknown GLA status";
+  }
+}
+
+const char* gla_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

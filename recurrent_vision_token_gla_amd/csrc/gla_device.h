@@ -1,0 +1,79 @@
+// Device-side helpers shared by the gfx950 kernels: scan-order index math,
+// per-batch direction codes, vector types for the matrix-core builtins, and
+// row loads/stores that convert between the storage type and half/float.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;          // 4 wave64 per workgroup
+constexpr int kMaxBatchPerLaunch = 1024;
+
+// Direction codes of up to kMaxBatchPerLaunch batch elements, 2 bits each,
+// passed by value in the kernel arguments (no device copy, graph-safe).
+struct DirPack {
+  uint32_t w[kMaxBatchPerLaunch / 16];
+  __host__ __device__ int get(int b) const { return (w[b >> 4] >> (2 * (b & 15))) & 3; }
+};
+
+// Raster index of the token at scan position t (GTR project page, "How GTR
+// Works": four scan orders over the patch grid). Left->right is raster
+// order; top->bottom walks columns left to right, each top to bottom;
+// right->left and bottom->top reverse those two sequences.
+__device__ __forceinline__ int scan_to_raster(int t, int T, int gh, int gw, int dir) {
+  if (dir & 1) t = T - 1 - t;               // R2L (1) and B2T (3) reverse
+  if (dir & 2) return (t % gh) * gw + t / gh;  // T2B (2) and B2T (3)
+  return t;
+}
+
+// ---- row loads of 8 consecutive elements --------------------------------
+__device__ __forceinline__ void load8(const half_t* p, float (&x)[8]) {
+  half8 h = *reinterpret_cast<const half8*>(p);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) x[c] = (float)h[c];
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) { x[c] = a[c]; x[c + 4] = b[c]; }
+}
+__device__ __forceinline__ half8 load8h(const half_t* p) {
+  return *reinterpret_cast<const half8*>(p);
+}
+__device__ __forceinline__ half8 load8h(const float* p) {
+  floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+  half8 h;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) { h[c] = (half_t)a[c]; h[c + 4] = (half_t)b[c]; }
+  return h;
+}
+
+// ---- row stores of 8 consecutive elements from float -----------------------
+__device__ __forceinline__ void store8(half_t* p, const float (&x)[8]) {
+  half8 h;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) h[c] = (half_t)x[c];
+  *reinterpret_cast<half8*>(p) = h;
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  floatx4 a = {x[0], x[1], x[2], x[3]};
+  floatx4 b = {x[4], x[5], x[6], x[7]};
+  *reinterpret_cast<floatx4*>(p) = a;
+  *reinterpret_cast<floatx4*>(p + 4) = b;
+}
+
+__device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace gla

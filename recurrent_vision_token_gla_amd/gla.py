@@ -1,0 +1,203 @@
+"""Thin ctypes binding over libgla_mi355x.so (C ABI in include/gla.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the forward runs in the library's HIP kernels. There is
+no fallback: if the library is not built, or a call fails, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgla_mi355x.so")
+
+L2R, R2L, T2B, B2T = 0, 1, 2, 3
+F16, F32 = 0, 1
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+
+# every symbol declared in include/gla.h
+EXPORTS = ["gla_abi_version", "gla_fwd_workspace_bytes", "gla_workspace_layout", "gla_fwd",
+           "gla_chunk_summaries", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
+           "gla_status_string", "gla_last_error_detail"]
+
+_lib = None
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class GLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.gla_status_string(status).decode()
+        detail = lib.gla_last_error_detail().decode()
+        super().__init__(f"{where}: {msg}" + (f" ({detail})" if detail and status == E_HIP else ""))
+        self.status = status
+
+
+def load():
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing; run "
+                           "__graft_entry__.build() or recurrent_vision_token_gla_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gla_abi_version.restype = _i32
+    lib.gla_fwd_workspace_bytes.restype = _sz
+    lib.gla_fwd_workspace_bytes.argtypes = [_i32] * 7
+    lib.gla_workspace_layout.restype = _i32
+    lib.gla_workspace_layout.argtypes = [_i32] * 7 + [ctypes.POINTER(_sz)] * 4
+    lib.gla_fwd.restype = _i32
+    lib.gla_fwd.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
+    lib.gla_chunk_summaries.restype = _i32
+    lib.gla_chunk_summaries.argtypes = [_vp] * 3 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
+    lib.gla_state_scan.restype = _i32
+    lib.gla_state_scan.argtypes = [_i32] * 7 + [_vp, _sz, _vp]
+    lib.gla_chunk_outputs.restype = _i32
+    lib.gla_chunk_outputs.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
+    lib.gla_scan_perm.restype = _i32
+    lib.gla_scan_perm.argtypes = [_vp, _i32, _i32, _i32, _vp]
+    lib.gla_status_string.restype = ctypes.c_char_p
+    lib.gla_status_string.argtypes = [_i32]
+    lib.gla_last_error_detail.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise GLAError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use float16 or float32")
+
+
+def _dirs(direction: Union[int, Sequence[int]], B: int):
+    if isinstance(direction, int):
+        vals = [direction] * B
+    else:
+        vals = [int(d) for d in direction]
+        if len(vals) != B:
+            raise ValueError(f"need one direction per batch element ({B}), got {len(vals)}")
+    arr = (ctypes.c_int32 * max(1, B))(*vals)
+    return arr
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def workspace_bytes(B, H, grid_h, grid_w, dk, dv, chunk=64) -> int:
+    return int(load().gla_fwd_workspace_bytes(B, H, grid_h, grid_w, dk, dv, chunk))
+
+
+def workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk=64):
+    """(off_U, off_a, off_S, total) byte offsets inside the workspace."""
+    vals = [_sz() for _ in range(4)]
+    _check(load().gla_workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk,
+                                       *[ctypes.byref(x) for x in vals]), "gla_workspace_layout")
+    return tuple(int(x.value) for x in vals)
+
+
+def alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk=64, device=None) -> torch.Tensor:
+    n = workspace_bytes(B, H, grid_h, grid_w, dk, dv, chunk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def _shapes(q, k, v, gk, grid_h, grid_w):
+    for name, t in (("q", q), ("k", k), ("v", v), ("gk", gk)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, T, H, D]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, T, H, D]")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, gk must share one dtype")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if T != grid_h * grid_w:
+        raise ValueError(f"T={T} but grid is {grid_h}x{grid_w}")
+    if k.shape != q.shape or gk.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("shape mismatch between q, k, gk [B,T,H,dk] and v [B,T,H,dv]")
+    return B, T, H, dk, dv
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
+        grid_h: int, grid_w: int, direction: Union[int, Sequence[int]] = L2R,
+        chunk: int = 64, out: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None,
+        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """o = key-only GLA forward along `direction` (int, or one per batch element)."""
+    B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
+    st = load().gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), out.data_ptr(),
+                        B, H, grid_h, grid_w, dk, dv, _dirs(direction, B), chunk, _dtype_code(q),
+                        workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _check(st, "gla_fwd")
+    return out
+
+
+def chunk_summaries(k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspace=None,
+                    stream=None) -> torch.Tensor:
+    """Phase 1 only; returns the workspace holding U and a."""
+    B, T, H, dk, dv = _shapes(k, k, v, gk, grid_h, grid_w)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, k.device)
+    st = load().gla_chunk_summaries(k.data_ptr(), v.data_ptr(), gk.data_ptr(), B, H, grid_h,
+                                    grid_w, dk, dv, _dirs(direction, B), chunk, _dtype_code(k),
+                                    workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _check(st, "gla_chunk_summaries")
+    return workspace
+
+
+def state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace, stream=None) -> torch.Tensor:
+    st = load().gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace.data_ptr(),
+                               workspace.numel(), _stream_ptr(stream))
+    _check(st, "gla_state_scan")
+    return workspace
+
+
+def chunk_outputs(q, k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspace=None,
+                  out=None, stream=None) -> torch.Tensor:
+    B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    st = load().gla_chunk_outputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                                  out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
+                                  _dirs(direction, B), chunk, _dtype_code(q),
+                                  workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _check(st, "gla_chunk_outputs")
+    return out
+
+
+def workspace_views(workspace: torch.Tensor, B, H, grid_h, grid_w, dk, dv, chunk=64):
+    """Views of U [B,H,N,dv,dk] f32, a [B,H,N,dk] f32, S [B,H,N,dv,dk] f16."""
+    off_U, off_a, off_S, _ = workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk)
+    N = -(-(grid_h * grid_w) // chunk)
+    n_us = B * H * N * dk * dv
+    U = workspace[off_U:off_U + 4 * n_us].view(torch.float32).view(B, H, N, dv, dk)
+    a = workspace[off_a:off_a + 4 * B * H * N * dk].view(torch.float32).view(B, H, N, dk)
+    S = workspace[off_S:off_S + 2 * n_us].view(torch.float16).view(B, H, N, dv, dk)
+    return U, a, S
+
+
+def scan_perm(grid_h: int, grid_w: int, direction: int, device="cuda", stream=None) -> torch.Tensor:
+    """Device-computed scan order (raster index per scan position), int32."""
+    perm = torch.empty(max(1, grid_h * grid_w), dtype=torch.int32, device=device)
+    st = load().gla_scan_perm(perm.data_ptr(), grid_h, grid_w, direction, _stream_ptr(stream))
+    _check(st, "gla_scan_perm")
+    return perm[:grid_h * grid_w]

@@ -1,0 +1,114 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/gla.h declares, and rejects bad arguments on the host before any HIP
+call. No call here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from recurrent_vision_token_gla_amd import gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(gla_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gla.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return gla.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(gla.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gla_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, 7):
+        s = lib.gla_status_string(st)
+        assert s and isinstance(s, bytes)
+    assert lib.gla_status_string(-3).startswith(b"GLA_E_WORKSPACE")
+    assert lib.gla_last_error_detail() == b""
+
+
+def test_workspace_bytes(lib):
+    # U (f32) + a (f32) + S (f16), each padded to 256 bytes
+    B, H, gh, gw, dk, dv, C = 1, 6, 40, 40, 64, 64, 64
+    N = 25
+    units = B * H * N
+    expect = units * dk * dv * 4 + units * dk * 4 + units * dk * dv * 2
+    assert gla.workspace_bytes(B, H, gh, gw, dk, dv, C) == expect
+    assert gla.workspace_bytes(0, H, gh, gw, dk, dv, C) == 0
+    assert gla.workspace_bytes(1, 1, 5, 7, 32, 32, 16) > 0
+    assert gla.workspace_bytes(1, 1, 8, 8, 48, 32, 16) == 0  # unsupported dk
+    off_U, off_a, off_S, total = gla.workspace_layout(B, H, gh, gw, dk, dv, C)
+    assert off_U == 0 and off_a % 256 == 0 and off_S % 256 == 0 and total == expect
+
+
+FAKE = 0x10000  # 256-aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, g=FAKE + 0x3000, o=FAKE + 0x4000,
+         B=1, H=1, gh=4, gw=4, dk=32, dv=32, dirs=(0,), chunk=16, dtype=0, ws=FAKE + 0x5000,
+         ws_bytes=0):
+    arr = (ctypes.c_int32 * max(1, len(dirs)))(*dirs) if dirs is not None else None
+    return lib.gla_fwd(q, k, v, g, o, B, H, gh, gw, dk, dv, arr, chunk, dtype, ws, ws_bytes, None)
+
+
+def test_argument_errors_before_any_launch(lib):
+    E_ARG, E_UNS, E_WS = gla.E_ARG, gla.E_UNSUPPORTED, gla.E_WORKSPACE
+    assert _fwd(lib, q=None) == E_ARG
+    assert _fwd(lib, o=None) == E_ARG
+    assert _fwd(lib, q=FAKE + 2) == E_ARG            # misaligned
+    assert _fwd(lib, B=-1) == E_ARG
+    assert _fwd(lib, gh=-3) == E_ARG
+    assert _fwd(lib, dtype=5) == E_ARG
+    assert _fwd(lib, dk=48) == E_UNS
+    assert _fwd(lib, dv=128) == E_UNS
+    assert _fwd(lib, chunk=48) == E_UNS
+    assert _fwd(lib, dirs=(4,)) == E_ARG
+    assert _fwd(lib, dirs=(-1,)) == E_ARG
+    assert _fwd(lib, dirs=None) == E_ARG
+    assert _fwd(lib, o=FAKE) == E_ARG                 # o aliases q
+    assert _fwd(lib, ws=None) == E_ARG
+    assert _fwd(lib, ws=FAKE + 0x5010) == E_ARG       # workspace not 256-aligned
+    need = gla.workspace_bytes(1, 1, 4, 4, 32, 32, 16)
+    assert _fwd(lib, ws_bytes=need - 1) == E_WS
+    assert _fwd(lib, B=2, dirs=(0, 9), ws_bytes=10 ** 9) == E_ARG
+    assert lib.gla_last_error_detail() == b""
+
+
+def test_empty_problems_are_noops(lib):
+    # nothing to compute: returns OK and does not look at the pointers
+    assert _fwd(lib, q=None, k=None, v=None, g=None, o=None, ws=None, B=0, dirs=None) == gla.OK
+    assert _fwd(lib, q=None, k=None, v=None, g=None, o=None, ws=None, H=0) == gla.OK
+    assert _fwd(lib, q=None, k=None, v=None, g=None, o=None, ws=None, gh=0) == gla.OK
+    assert lib.gla_scan_perm(None, 0, 5, 0, None) == gla.OK
+
+
+def test_phase_entry_points_validate(lib):
+    arr = (ctypes.c_int32 * 1)(0)
+    assert lib.gla_chunk_summaries(None, FAKE, FAKE, 1, 1, 4, 4, 32, 32, arr, 16, 0, FAKE, 10 ** 6,
+                                   None) == gla.E_ARG
+    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 16, FAKE, 1, None) == gla.E_WORKSPACE
+    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 24, FAKE, 10 ** 6, None) == gla.E_UNSUPPORTED
+    assert lib.gla_chunk_outputs(FAKE, FAKE + 0x100, FAKE + 0x200, FAKE + 0x300, FAKE + 0x100, 1, 1,
+                                 4, 4, 32, 32, arr, 16, 0, FAKE, 10 ** 6, None) == gla.E_ARG
+    assert lib.gla_scan_perm(FAKE, 4, 4, 7, None) == gla.E_ARG
+    assert lib.gla_scan_perm(None, 4, 4, 0, None) == gla.E_ARG
+    assert lib.gla_scan_perm(FAKE + 1, 4, 4, 0, None) == gla.E_ARG
