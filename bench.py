@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise key-only GLA forward on one MI355X.
+
+Metric: forward tokens/s (fp16) on the 640x640-image workload (B=1, 40x40
+stride-16 grid = 1,600 tokens, H=6, dk=dv=64, chunk 64, one call per scan
+direction), with the 1280x1280 workload (6,400 tokens) reported beside it,
+and the fraction of the HBM roofline reached.
+
+A step is one pass of the workload: one gla_fwd call per scan direction on
+that call's own seeded inputs, already resident in device memory. Steps are
+replayed from a captured HIP graph and timed with events on the launching
+stream, mirroring the pages' protocol of event timing under graph replay
+(GTR project page, "Accuracy-Latency Frontier"). One JSON line is printed.
+
+  python bench.py [--steps K] [--warmup W] [--workload I] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunkwise GLA fwd tokens/s (fp16) at 1600/6400 tokens; % of roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCES = ["gla_kernels.hip", "gla_device.h", "gla_launch.h"]
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "recurrent_vision_token_gla_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def per_unit_bytes(w):
+    """Algorithmic bytes of the whole forward per (token, head): read q, k, gk
+    (dk each) and v (dv), write o (dv)."""
+    e = 2 if w.dtype == "f16" else 4
+    return (3 * w.dk + 2 * w.dv) * e
+
+
+def phase_bytes(w):
+    """Bytes each phase must move in the three-kernel schedule, per launch.
+
+    summaries: read k, gk, v; write U (f32 dk*dv) and a (f32 dk) per chunk-head
+    scan:      read U and a; write S (f16 dk*dv) per chunk-head
+    outputs:   read q, k, gk, v and S; write o
+    """
+    e = 2 if w.dtype == "f16" else 4
+    th = w.B * w.T * w.H
+    ch = w.B * w.H * math.ceil(w.T / w.chunk)
+    return {
+        "summaries": th * (2 * w.dk + w.dv) * e + ch * (4 * w.dk * w.dv + 4 * w.dk),
+        "scan": ch * (4 * w.dk * w.dv + 4 * w.dk + 2 * w.dk * w.dv),
+        "outputs": th * (3 * w.dk + 2 * w.dv) * e + ch * 2 * w.dk * w.dv,
+    }
+
+
+def load_traffic(kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch from profiles/traffic.json, or None
+    if absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for r in rec.get("entries", []):
+        if r.get("kernel") == kernel and r.get("workload") == workload:
+            if r.get("source_sha") != source_sha():
+                return None
+            return r.get("hbm_bytes_per_launch")
+    return None
+
+
+def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
+    dev = torch.device("cuda:0")
+    calls = []
+    for c in range(w.calls):
+        q, k, v, g = W.workload_inputs(w, c)
+        tq, tk, tv, tg = (torch.from_numpy(x).to(dev) for x in (q, k, v, g))
+        calls.append(dict(q=tq, k=tk, v=tv, g=tg, dirs=w.directions(c),
+                          out=torch.empty_like(tv), host=(q, k, v, g)))
+    ws = gla.alloc_workspace(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(s=None):
+        for c in calls:
+            gla.fwd(c["q"], c["k"], c["v"], c["g"], w.grid_h, w.grid_w, c["dirs"], w.chunk,
+                    out=c["out"], workspace=ws, stream=s)
+
+    step()
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                step(s)
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / steps
+
+    # median single-step latency (event pair per step)
+    lat = []
+    for _ in range(min(50, max(10, steps // 4))):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        b.synchronize()
+        lat.append(a.elapsed_time(b) * 1e3)
+
+    # per-phase kernel durations: each phase alone, back to back, events on
+    # the stream it is launched on (torch's current stream)
+    c0 = calls[0]
+    phases = {
+        "summaries": lambda: gla.chunk_summaries(c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
+                                                 c0["dirs"], w.chunk, workspace=ws),
+        "scan": lambda: gla.state_scan(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, ws),
+        "outputs": lambda: gla.chunk_outputs(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h,
+                                             w.grid_w, c0["dirs"], w.chunk, workspace=ws,
+                                             out=c0["out"]),
+    }
+    phase_us = {}
+    for name, fn in phases.items():
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(timing_reps):
+            fn()
+        b.record()
+        b.synchronize()
+        phase_us[name] = a.elapsed_time(b) * 1e3 / timing_reps
+    return dict(calls=calls, ms_per_step=ms_per_step, wall_s=wall, lat_us=lat,
+                phase_us=phase_us, ws=ws)
+
+
+def parity_check(w, res, oracle, np, max_bh=4):
+    """Max relative error of the benchmarked outputs against the oracle, on
+    a sample of (batch, head) slices of every call."""
+    errs = []
+    for c in res["calls"]:
+        q, k, v, g = c["host"]
+        o = c["out"].double().cpu().numpy()
+        bhs = [(b, h) for b in range(w.B) for h in range(w.H)][:max_bh]
+        for b, h in bhs:
+            sl = lambda x: x[b:b + 1, :, h:h + 1]
+            ref = oracle.gla_forward(sl(q), sl(k), sl(v), sl(g), w.grid_h, w.grid_w,
+                                     [c["dirs"][b]])
+            errs.append(float(np.max(np.abs(o[b:b + 1, :, h:h + 1] - ref)) / np.max(np.abs(ref))))
+    return max(errs)
+
+
+def cpu_baseline(w, res, oracle, target_s=3.0):
+    """The oracle, as it stands, timed on the host cores on the same inputs."""
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for c in res["calls"]:
+            q, k, v, g = c["host"]
+            oracle.gla_forward(q, k, v, g, w.grid_h, w.grid_w, c["dirs"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 20:
+            break
+    tokens = reps * w.calls * w.B * w.T
+    return {"value": tokens / el, "unit": "tokens/s", "cores": oracle.oracle_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full step(s) of {w.name} ({w.calls} calls, all heads), "
+                      f"{el:.2f} s wall"}
+
+
+def summarize(w, res):
+    tokens_step = w.calls * w.B * w.T
+    value = tokens_step / (res["ms_per_step"] * 1e-3)
+    th_call = w.B * w.T * w.H
+    path_bytes_call = th_call * per_unit_bytes(w)
+    call_us = res["ms_per_step"] * 1e3 / w.calls
+    pb = phase_bytes(w)
+    dom = max(res["phase_us"], key=res["phase_us"].get)
+    ach = pb[dom] / (res["phase_us"][dom] * 1e-6) / 1e9
+    return {
+        "value": value,
+        "call_us": call_us,
+        "median_step_latency_us": statistics.median(res["lat_us"]),
+        "path_roofline": {"bound": "hbm", "achieved": path_bytes_call / (call_us * 1e-6) / 1e9,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": path_bytes_call / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "bytes_per_call": path_bytes_call},
+        "dominant": dom,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS,
+                     "traffic": load_traffic(dom, w.name),
+                     "kernel": dom, "algorithmic_bytes_per_launch": pb[dom],
+                     "avg_launch_us": res["phase_us"][dom]},
+        "phase_us": res["phase_us"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, help="index into workloads.WORKLOADS")
+    ap.add_argument("--all", action="store_true", help="also run the batched and stack workloads")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-also", action="store_true", help="only the selected workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; there is no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from recurrent_vision_token_gla_amd import gla
+    from recurrent_vision_token_gla_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gla.load()
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: 3 copies of {n} bytes", file=sys.stderr, flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
+
+    w = W.WORKLOADS[args.workload]
+    print(f"# bench: workload {w.index} {w.name} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    res = run_workload(w, args.steps, args.warmup, not args.no_graph, torch, gla, W)
+    s = summarize(w, res)
+    print(f"# {w.name}: {s['value']:.4g} tokens/s, {s['call_us']:.2f} us/call, "
+          f"path {100 * s['path_roofline']['frac']:.1f}% of HBM roofline, phases "
+          + ", ".join(f"{k} {v:.2f} us" for k, v in s["phase_us"].items()),
+          file=sys.stderr, flush=True)
+
+    import oracle
+    parity = parity_check(w, res, oracle, np)
+    print(f"# parity max rel err (sampled) {parity:.3e}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, res, oracle)
+        print(f"# cpu oracle {cpu['value']:.4g} tokens/s on {cpu['cores']} threads",
+              file=sys.stderr, flush=True)
+
+    also = []
+    extra = [2] if args.workload == 1 and not args.no_also else []
+    if args.all:
+        extra += [i for i in (2, 3, 4) if i != args.workload and i not in extra]
+    for i in extra:
+        wi = W.WORKLOADS[i]
+        ri = run_workload(wi, max(10, args.steps // 4), max(3, args.warmup // 4),
+                          not args.no_graph, torch, gla, W)
+        si = summarize(wi, ri)
+        print(f"# {wi.name}: {si['value']:.4g} tokens/s, {si['call_us']:.2f} us/call, path "
+              f"{100 * si['path_roofline']['frac']:.1f}% of HBM roofline, phases "
+              + ", ".join(f"{k} {v:.2f} us" for k, v in si["phase_us"].items()),
+              file=sys.stderr, flush=True)
+        also.append({"workload": wi.name, "tokens_per_call": wi.B * wi.T,
+                     "value": si["value"], "unit": "tokens/s", "us_per_call": si["call_us"],
+                     "path_roofline_frac": si["path_roofline"]["frac"],
+                     "dominant": si["dominant"], "dominant_frac": si["roofline"]["frac"],
+                     "phase_us": si["phase_us"]})
+        del ri
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": s["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "grid": f"{w.grid_h}x{w.grid_w}",
+                   "tokens_per_call": w.B * w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "calls_per_step": w.calls, "dir_mode": w.dir_mode,
+                   "timing": "eager" if args.no_graph else "graph_replay"},
+        "roofline": s["roofline"],
+        "path_roofline": s["path_roofline"],
+        "median_step_latency_us": s["median_step_latency_us"],
+        "phase_us": s["phase_us"],
+        "parity_max_rel_err": parity,
+        "cpu_baseline": cpu,
+        "also": also,
+        "kernel_source_sha": source_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -201,228 +201,290 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const float* __restrict_
 
 // ===========================================================================
 // Phase 3: chunk outputs. One workgroup per (chunk n, head h, batch b).
-//   O = A V + Q^ S_n,   A = causal decayed score tile (in LDS, half)
+//   O = A V + Q^ S_n,   A = causal decayed score tile
+//
+// Wave w owns query sub-block I = w (tokens 16I..16I+15). A lane holds one
+// token row (lr = lane % 16) and 8*DK/32 key dims d = 32*ks + 8*(lane/16) + c,
+// which is exactly the operand layout of the 16x16x32 matrix-core product, so
+// the per-element factors are computed in registers and fed to the matrix
+// cores directly. Within a sub-block, with s_i = sum of g2 over its tokens up
+// to i and tot = s_15 (all log2):
+//   Q~ = q 2^(s_i)   K~ = k 2^(tot - s_i)   Q^ = Q~ 2^(beta_I)
+// Score sub-blocks are produced transposed (A^T = K Q^T), so each lane ends
+// up holding A[i = lr][j = 4*(lane/16) + r], the operand layout of the 16x16x16
+// product A V: the score tile stays in registers, never round-tripping LDS.
+//   off-diagonal J < I: A_IJ = (Q~_I * m_IJ) K~_J^T, m_IJ = 2^(beta_I - e_J)
+//   diagonal:           A_II = Q' K'^T with Q' = q 2^(s_i - s_7),
+//                       K' = k 2^(s_7 - s_j): one reference at the 8th token.
+// The diagonal block uses half operands when no key dim decays by more than
+// 2^8 over a sub-block, fp32 operands up to 2^120, and beyond that (checked
+// per tile) sums every entry directly from 2^(s_i - s_j).
 // ===========================================================================
+__device__ __forceinline__ float row_scan16(float x) {
+  // inclusive prefix sum over the 16 lanes of each DPP row
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+  return x;
+}
+
+__device__ __forceinline__ floatx4 mfma16x16x16(half4 a, half4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+struct OutStage;
+template <>
+struct OutStage<half_t> {
+  typedef half_t type;
+};
+template <>
+struct OutStage<float> {
+  typedef float type;
+};
+
 template <int DK, int DV, int C, typename InT>
-__global__ __launch_bounds__(kThreads) void output_kernel(
+__global__ __launch_bounds__(kThreads, 3) void output_kernel(
     const InT* __restrict__ qp, const InT* __restrict__ kp, const InT* __restrict__ vp,
     const InT* __restrict__ gp, const half_t* __restrict__ Sws, InT* __restrict__ op, int T,
     int H, int N, int gh, int gw, DirPack dirs) {
-  using G = Geo<DK, DV, C>;
-  constexpr int CP = G::CP, NB = G::NB;
-  constexpr int DMAX = DK > DV ? DK : DV;
-  constexpr int VA = (C * G::VSTR > C * G::TSTR) ? C * G::VSTR : C * G::TSTR;
-  __shared__ __attribute__((aligned(16))) float sAl[C][DK];      // g2, then 2^(g2)
-  __shared__ __attribute__((aligned(16))) float sQt[C * DMAX];   // Q~ (f32), then O staging
-  __shared__ __attribute__((aligned(16))) half_t sQ[C][G::KSTR];
-  __shared__ __attribute__((aligned(16))) half_t sK[C][G::KSTR];
-  __shared__ __attribute__((aligned(16))) half_t sKt[C][G::KSTR];  // K~ row-major
-  __shared__ __attribute__((aligned(16))) half_t sQh[C][G::KSTR];  // Q^ row-major
-  __shared__ __attribute__((aligned(16))) half_t sVA[VA];          // V rows, then A tile
-  __shared__ __attribute__((aligned(16))) half_t sVt[DV][G::TSTR];
-  __shared__ float sBnd[NB + 1][DK];
-  __shared__ float sM[G::NPAIR > 0 ? G::NPAIR : 1][DK];
-  __shared__ float sTot[G::NSEG][DK];
+  constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16;
+  constexpr int NPAIR = NB * (NB - 1) / 2;
+  constexpr int KSTR = DK + 8;  // halves, rows of K~ and S^T
+  constexpr int VSTR = C + 8;   // halves, rows of V^T
+  constexpr int OSTR = DV + 8;  // rows of the output staging tile
+  constexpr float kHalfRange = 8.f, kF32Range = 120.f;  // log2 decay per sub-block
+  typedef typename OutStage<InT>::type OT;
+  __shared__ __attribute__((aligned(16))) half_t sKt[C][KSTR];
+  __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
+  __shared__ __attribute__((aligned(16))) half_t sS[DV][KSTR];
+  __shared__ __attribute__((aligned(16))) OT sO[C][OSTR];
+  __shared__ float sTot[NB][DK], sS7[NB][DK];
+  __shared__ float sEb[NB][DK], sR1[NB][DK], sR2[NB][DK];
+  __shared__ float sM[NPAIR > 0 ? NPAIR : 1][DK];
   __shared__ int sRow[C];
-  half_t (*sV)[G::VSTR] = reinterpret_cast<half_t (*)[G::VSTR]>(sVA);
-  half_t (*sA)[G::TSTR] = reinterpret_cast<half_t (*)[G::TSTR]>(sVA);
+  __shared__ int sTier;
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
   const int tok0 = n * C;
   const int L = min(C, T - tok0);
   if (tid < C) sRow[tid] = tid < L ? scan_to_raster(tok0 + tid, T, gh, gw, dirs.get(b)) : -1;
+  if (tid == 0) sTier = 0;
   __syncthreads();
 
-  // -- load q, k, gk rows (dk) and v rows (dv); padding rows are zero
-  for (int u = tid; u < C * (DK / 8); u += kThreads) {
-    const int r = u / (DK / 8), c8 = (u % (DK / 8)) * 8;
-    float g8[8];
-    half8 q8, k8;
-    if (sRow[r] >= 0) {
-      const long row = ((long)b * T + sRow[r]) * H + h;
-      load8(gp + row * DK + c8, g8);
-      q8 = load8h(qp + row * DK + c8);
-      k8 = load8h(kp + row * DK + c8);
-    } else {
+  // -- this wave's token rows of q, k, gk in the operand layout
+  const bool owner = wave < NB;
+  const int I = wave;
+  const int t = 16 * I + lr;
+  float qf[NEL], kf[NEL], sc[NEL];
+  if (owner) {
+    const int row = sRow[t];
+    const long base = ((long)b * T + row) * H + h;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) { g8[c] = 0.f; q8[c] = k8[c] = (half_t)0.f; }
-    }
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (row >= 0) {
+        const half8 q8 = load8h(qp + base * DK + 32 * ks + lk);
+        const half8 k8 = load8h(kp + base * DK + 32 * ks + lk);
+        float g8[8];
+        load8(gp + base * DK + 32 * ks + lk, g8);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) sAl[r][c8 + c] = g8[c] * kLog2e;
-    *reinterpret_cast<half8*>(&sQ[r][c8]) = q8;
-    *reinterpret_cast<half8*>(&sK[r][c8]) = k8;
-  }
-  for (int u = tid; u < C * (DV / 8); u += kThreads) {
-    const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
-    half8 v8;
-    if (sRow[r] >= 0) {
-      const long row = ((long)b * T + sRow[r]) * H + h;
-      v8 = load8h(vp + row * DV + c8);
-    } else {
+        for (int c = 0; c < 8; ++c) {
+          qf[8 * ks + c] = (float)q8[c];
+          kf[8 * ks + c] = (float)k8[c];
+          sc[8 * ks + c] = g8[c] * kLog2e;
+        }
+      } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v8[c] = (half_t)0.f;
-    }
-    *reinterpret_cast<half8*>(&sV[r][c8]) = v8;
-  }
-  __syncthreads();
-
-  // -- cumsum; g2 -> per-token decay 2^(g2) in place; sub-block boundaries
-  const int d = tid % DK, seg = tid / DK;
-  float p[G::SEGLEN];
-  float run = 0.f;
-#pragma unroll
-  for (int i = 0; i < G::SEGLEN; ++i) {
-    const int t = seg * G::SEGLEN + i;
-    const float g2 = sAl[t][d];
-    run += g2;
-    p[i] = run;
-    sAl[t][d] = exp2f(g2);
-  }
-  sTot[seg][d] = run;
-  // V transposed into [e][token] (reads sV, written before the last barrier)
-  for (int u = tid; u < DV * (C / 8); u += kThreads) {
-    const int e = u % DV, j8 = (u / DV) * 8;
-    half8 x;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) x[c] = sV[j8 + c][e];
-    *reinterpret_cast<half8*>(&sVt[e][j8]) = x;
-  }
-  if constexpr (CP > C) {
-    for (int u = tid; u < DV * (CP - C); u += kThreads)
-      sVt[u / (CP - C)][C + u % (CP - C)] = (half_t)0.f;
-  }
-  __syncthreads();
-  float off = 0.f;
-#pragma unroll
-  for (int s = 0; s < G::NSEG; ++s)
-    if (s < seg) off += sTot[s][d];
-  if (seg == 0) sBnd[0][d] = 0.f;
-  if (((seg + 1) * G::SEGLEN) % 16 == 0) sBnd[(seg + 1) * G::SEGLEN / 16][d] = off + run;
-  __syncthreads();
-
-  // -- factors: Q~ (f32), Q^ (half), K~ (half), and the pair factors m_IJ
-  {
-    const int I = (seg * G::SEGLEN) / 16;  // the segment lies in one sub-block
-    const float beta = sBnd[I][d], eI = sBnd[I + 1][d];
-    const float ebeta = exp2f(beta);
-#pragma unroll
-    for (int i = 0; i < G::SEGLEN; ++i) {
-      const int t = seg * G::SEGLEN + i;
-      const float bt = off + p[i];
-      const float qt = (float)sQ[t][d] * exp2f(bt - beta);
-      sQt[t * DK + d] = qt;
-      sQh[t][d] = (half_t)(qt * ebeta);
-      sKt[t][d] = (half_t)((float)sK[t][d] * exp2f(eI - bt));
-    }
-    if (seg == 0) {
-      for (int I2 = 1; I2 < NB; ++I2)
-        for (int J = 0; J < I2; ++J)
-          sM[I2 * (I2 - 1) / 2 + J][d] = exp2f(sBnd[I2][d] - sBnd[J + 1][d]);
-    }
-  }
-  __syncthreads();
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lk = 8 * (lane >> 4);
-
-  // -- strict upper triangle of the tile (causal mask), padding columns included
-  for (int u = tid; u < C * CP; u += kThreads) {
-    const int row = u / CP, col = u % CP;
-    if (col > row) sA[row][col] = (half_t)0.f;
-  }
-
-  // -- diagonal sub-blocks, exact: A_ij = sum_d q_i k_j prod_{r=j+1..i} 2^(g2_r)
-  //    A wave owns one row index i of every diagonal sub-block at a time
-  //    (rows {w, 7-w, 8+w, 15-w}: equal work per wave); a lane owns four key
-  //    dims of one sub-block; j runs from i down to 0 carrying the product.
-  {
-    constexpr int LPB = DK / 4;  // lanes per sub-block
-    const int I = lane / LPB, dq = lane % LPB;
-    const bool active = I < NB;
-#pragma unroll 1
-    for (int ri = 0; ri < 4; ++ri) {
-      const int i = (ri & 1) ? ((ri & 2) ? 15 - wave : 7 - wave) : ((ri & 2) ? 8 + wave : wave);
-      float u4[4] = {0.f, 0.f, 0.f, 0.f};
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) u4[c] = (float)sQ[16 * I + i][4 * dq + c];
+        for (int c = 0; c < 8; ++c) qf[8 * ks + c] = kf[8 * ks + c] = sc[8 * ks + c] = 0.f;
       }
-#pragma unroll 1
-      for (int j = i; j >= 0; --j) {
-        float acc = 0.f;
-        if (active) {
-          const half4 k4 = *reinterpret_cast<const half4*>(&sK[16 * I + j][4 * dq]);
-          const floatx4 al = *reinterpret_cast<const floatx4*>(&sAl[16 * I + j][4 * dq]);
+    }
+  }
+  // -- V rows transposed into V^T, and the entering state S^T, through LDS
+  {
+    const long bhn = ((long)b * H + h) * N + n;
+    const half_t* Sb = Sws + bhn * (long)(DV * DK);
+    for (int u = tid; u < DV * (DK / 8); u += kThreads) {
+      const int e = u / (DK / 8), d8 = (u % (DK / 8)) * 8;
+      *reinterpret_cast<half8*>(&sS[e][d8]) = load8h(Sb + e * DK + d8);
+    }
+    for (int u = tid; u < C * (DV / 8); u += kThreads) {
+      const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
+      half8 v8;
+      if (sRow[r] >= 0) {
+        v8 = load8h(vp + (((long)b * T + sRow[r]) * H + h) * DV + c8);
+      } else {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            acc += u4[c] * (float)k4[c];
-            u4[c] *= al[c];
-          }
+        for (int c = 0; c < 8; ++c) v8[c] = (half_t)0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sVt[c8 + c][r] = v8[c];
+    }
+  }
+
+  // -- in-sub-block inclusive cumsum along tokens (DPP row scan)
+  if (owner) {
+#pragma unroll
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]);
+    if (lr == 15 || lr == 7) {
+#pragma unroll
+      for (int e = 0; e < NEL; ++e) {
+        const int d = 32 * (e / 8) + lk + (e % 8);
+        if (lr == 15) sTot[I][d] = sc[e];
+        else sS7[I][d] = sc[e];
+      }
+    }
+  }
+  __syncthreads();
+
+  // -- per (sub-block, key dim) factors, one key dim per thread
+  if (tid < NB * DK) {
+    const int I2 = tid / DK, d = tid % DK;
+    float beta = 0.f;
+    for (int J = 0; J < I2; ++J) beta += sTot[J][d];
+    const float tot = sTot[I2][d], s7 = sS7[I2][d];
+    sEb[I2][d] = exp2f(beta);
+    sR1[I2][d] = exp2f(-s7);
+    sR2[I2][d] = exp2f(s7 - tot);
+    float acc = 0.f;  // log2 of m_{I2,J} for J = I2-1, I2-2, ...
+    for (int J = I2 - 1; J >= 0; --J) {
+      sM[I2 * (I2 - 1) / 2 + J][d] = exp2f(acc);
+      acc += sTot[J][d];
+    }
+    const float range = -tot;
+    if (!(range <= kF32Range)) atomicMax(&sTier, 2);
+    else if (!(range <= kHalfRange)) atomicMax(&sTier, 1);
+  }
+  // -- per-element factors; K~ goes to LDS for the other sub-blocks
+  float qt[NEL], kt[NEL];
+  if (owner) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      half8 k8;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int e = 8 * ks + c;
+        const float tot = sTot[I][32 * ks + lk + c];
+        qt[e] = qf[e] * exp2f(sc[e]);
+        kt[e] = kf[e] * exp2f(tot - sc[e]);
+        k8[c] = (half_t)kt[e];
+      }
+      *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = k8;
+    }
+  }
+  __syncthreads();
+
+  if (owner) {
+    const int tier = sTier;
+    // -- diagonal sub-block, transposed: acc[r] = A[i = lr][j = 4*lq + r]
+    floatx4 dacc = {0.f, 0.f, 0.f, 0.f};
+    if (tier == 0) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        half8 qa, ka;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int e = 8 * ks + c, d = 32 * ks + lk + c;
+          qa[c] = (half_t)(qt[e] * sR1[I][d]);
+          ka[c] = (half_t)(kt[e] * sR2[I][d]);
+        }
+        dacc = mfma16x16x32(ka, qa, dacc);
+      }
+    } else if (tier == 1) {
+#pragma unroll
+      for (int e = 0; e < NEL; ++e) {
+        const int d = 32 * (e / 8) + lk + (e % 8);
+        dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[e] * sR2[I][d], qt[e] * sR1[I][d], dacc,
+                                                    0, 0, 0);
+      }
+    } else {
+      // every entry directly: A_ij = sum_d q_i k_j 2^(s_i - s_j)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < NEL; ++e) {
+          const float kj = __shfl(kf[e], (lane & 48) | j);
+          const float sj = __shfl(sc[e], (lane & 48) | j);
+          part += qf[e] * kj * exp2f(sc[e] - sj);
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if ((j >> 2) == lq) dacc[j & 3] = part;
+      }
+    }
+    half4 A[NB];
+    half4 adiag;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) adiag[r] = (half_t)((4 * lq + r <= lr) ? dacc[r] : 0.f);
+#pragma unroll
+    for (int J = 0; J < NB; ++J)
+      if (J == I) A[J] = adiag;
+    // -- off-diagonal sub-blocks J < I
+#pragma unroll
+    for (int J = 0; J < NB - 1; ++J) {
+      if (J < I) {
+        const int pr = I * (I - 1) / 2 + J;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          half8 qm;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) qm[c] = (half_t)(qt[8 * ks + c] * sM[pr][32 * ks + lk + c]);
+          const half8 ka = *reinterpret_cast<const half8*>(&sKt[16 * J + lr][32 * ks + lk]);
+          acc = mfma16x16x32(ka, qm, acc);
         }
 #pragma unroll
-        for (int o = LPB / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-        if (active && dq == 0) sA[16 * I + i][16 * I + j] = (half_t)acc;
+        for (int r = 0; r < 4; ++r) A[J][r] = (half_t)acc[r];
       }
     }
-  }
-
-  // -- off-diagonal sub-blocks I > J on the matrix cores
-  for (int pr = wave; pr < G::NPAIR; pr += 4) {
-    int I = 1;
-    while ((I + 1) * I / 2 <= pr) ++I;
-    const int J = pr - I * (I - 1) / 2;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // -- O_I = sum_{J<=I} A_IJ V_J + Q^_I S
+    half8 qh[NKS];
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const int d0 = 32 * ks + lk;
-      half8 a;
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        a[c] = (half_t)(sQt[(16 * I + lr) * DK + d0 + c] * sM[pr][d0 + c]);
-      const half8 bb = *reinterpret_cast<const half8*>(&sKt[16 * J + lr][d0]);
-      acc = mfma16x16x32(a, bb, acc);
-    }
+      for (int c = 0; c < 8; ++c) qh[ks][c] = (half_t)(qt[8 * ks + c] * sEb[I][32 * ks + lk + c]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sA[16 * I + 4 * (lane >> 4) + r][16 * J + lr] = (half_t)acc[r];
-  }
-  __syncthreads();
-
-  // -- O = A V + Q^ S_n on the matrix cores; stage O (f32) in LDS
-  constexpr int NE = DV / 16;
-  const long bhn = ((long)b * H + h) * N + n;
-  const half_t* Sb = Sws + bhn * (long)(DV * DK);
-  float* sO = sQt;  // Q~ is no longer read
-  for (int blk = wave; blk < NB * NE; blk += 4) {
-    const int I = blk / NE, E = blk % NE;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int E = 0; E < NE; ++E) {
+      // one accumulation chain of a single product shape (16x16x16) per value
+      // block: the readout contracts four key dims per lane group per step
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < CP / 32; ++ks) {
-      if (32 * ks <= 16 * I + 15) {
-        const half8 a = *reinterpret_cast<const half8*>(&sA[16 * I + lr][32 * ks + lk]);
-        const half8 bb = *reinterpret_cast<const half8*>(&sVt[16 * E + lr][32 * ks + lk]);
-        acc = mfma16x16x32(a, bb, acc);
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const half4 sb =
+              *reinterpret_cast<const half4*>(&sS[16 * E + lr][32 * ks + lk + 4 * hh]);
+          const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
+                              : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
+          acc = mfma16x16x16(qa, sb, acc);
+        }
       }
-    }
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const half8 a = *reinterpret_cast<const half8*>(&sQh[16 * I + lr][32 * ks + lk]);
-      const half8 bb = load8h(Sb + (16 * E + lr) * DK + 32 * ks + lk);
-      acc = mfma16x16x32(a, bb, acc);
-    }
+      for (int J = 0; J < NB; ++J) {
+        if (J <= I) {
+          const half4 vb = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
+          acc = mfma16x16x16(A[J], vb, acc);
+        }
+      }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sO[(16 * I + 4 * (lane >> 4) + r) * DV + 16 * E + lr] = acc[r];
+      for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (OT)acc[r];
+    }
   }
   __syncthreads();
 
   // -- scatter rows back to their raster positions
   for (int u = tid; u < C * (DV / 8); u += kThreads) {
     const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
-    if (sRow[r] < 0) continue;
-    float x[8];
+    if (sRow[r] >= 0) {
+      float x[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) x[c] = sO[r * DV + c8 + c];
-    store8(op + (((long)b * T + sRow[r]) * H + h) * DV + c8, x);
+      for (int c = 0; c < 8; ++c) x[c] = (float)sO[r][c8 + c];
+      store8(op + (((long)b * T + sRow[r]) * H + h) * DV + c8, x);
+    }
   }
 }
 
