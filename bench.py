@@ -51,7 +51,7 @@ def per_unit_bytes(w):
 def phase_bytes(w):
     """Bytes each phase must move in the three-kernel schedule, per launch.
 
-    summaries: read k, gk, v; write U (f32 dk*dv) and a (f32 dk) per chunk-head
+    summaries: read k, gk, v; write U (f16 dk*dv) and a (f32 dk) per chunk-head
     scan:      read U and a; write S (f16 dk*dv) per chunk-head
     outputs:   read q, k, gk, v and S; write o
     """
@@ -59,8 +59,8 @@ def phase_bytes(w):
     th = w.B * w.T * w.H
     ch = w.B * w.H * math.ceil(w.T / w.chunk)
     return {
-        "summaries": th * (2 * w.dk + w.dv) * e + ch * (4 * w.dk * w.dv + 4 * w.dk),
-        "scan": ch * (4 * w.dk * w.dv + 4 * w.dk + 2 * w.dk * w.dv),
+        "summaries": th * (2 * w.dk + w.dv) * e + ch * (2 * w.dk * w.dv + 4 * w.dk),
+        "scan": ch * (2 * w.dk * w.dv + 4 * w.dk + 2 * w.dk * w.dv),
         "outputs": th * (3 * w.dk + 2 * w.dv) * e + ch * 2 * w.dk * w.dv,
     }
 

@@ -82,7 +82,7 @@ size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk,
 
 /* Byte offsets, within the workspace, of the three intermediate arrays, so
  * that callers (tests) can inspect them after the phase calls below:
- *   U : float [B][H][N][dv][dk]   chunk summaries, stored transposed (row e)
+ *   U : half  [B][H][N][dv][dk]   chunk summaries, stored transposed (row e)
  *   a : float [B][H][N][dk]       per-chunk total decay exp(sum of gk)
  *   S : half  [B][H][N][dv][dk]   state entering each chunk, transposed
  * with N = ceil(T / chunk). Returns GLA_OK or GLA_E_ARG/GLA_E_UNSUPPORTED. */

@@ -28,136 +28,159 @@
 namespace gla {
 namespace {
 
-template <int DK, int DV, int C>
-struct Geo {
-  static constexpr int CP = C < 32 ? 32 : C;  // token extent padded to MFMA depth
-  static constexpr int KSTR = DK + 8;         // row stride (halves), [C][DK] tiles
-  static constexpr int VSTR = DV + 8;         // row stride (halves), [C][DV] tiles
-  static constexpr int TSTR = CP + 8;         // row stride (halves), [D][CP] tiles
-  static constexpr int NSEG = kThreads / DK;  // token segments of the cumsum
-  static constexpr int SEGLEN = C / NSEG;     // tokens per segment
-  static constexpr int NB = C / 16;           // 16-token sub-blocks per chunk
-  static constexpr int NPAIR = NB * (NB - 1) / 2;
-  static_assert(SEGLEN >= 1 && 16 % SEGLEN == 0, "segment must tile a sub-block");
-  static_assert(C % 16 == 0 && DK % 32 == 0 && DV % 16 == 0, "shape");
-};
 
-// ===========================================================================
-// Phase 1: chunk summaries. One workgroup per (chunk n, head h, batch b).
-//   U^T[e][d] = sum_j V[j][e] * K^[j][d]   (stored transposed, row e)
-//   a[d]      = 2^(B[d])
-// ===========================================================================
-template <int DK, int DV, int C, typename InT>
-__global__ __launch_bounds__(kThreads) void summary_kernel(
-    const InT* __restrict__ kp, const InT* __restrict__ vp, const InT* __restrict__ gp,
-    float* __restrict__ Uws, float* __restrict__ Aws, int T, int H, int N, int gh, int gw,
-    DirPack dirs) {
-  using G = Geo<DK, DV, C>;
-  __shared__ __attribute__((aligned(16))) float sG[C][DK];
-  __shared__ __attribute__((aligned(16))) half_t sK[C][G::KSTR];
-  __shared__ __attribute__((aligned(16))) half_t sV[C][G::VSTR];
-  __shared__ __attribute__((aligned(16))) half_t sKt[DK][G::TSTR];
-  __shared__ __attribute__((aligned(16))) half_t sVt[DV][G::TSTR];
-  __shared__ float sTot[G::NSEG][DK];
-  __shared__ int sRow[C];
+// ---------------------------------------------------------------------------
+// Helpers shared by the phase kernels.
+// ---------------------------------------------------------------------------
+// exp2 on the transcendental unit. Results below 2^-126 flush to zero; every
+// factor built with it multiplies a term that is then negligible.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ float row_scan16(float x) {
+  // inclusive prefix sum over the 16 lanes of each DPP row
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+  return x;
+}
+
+__device__ __forceinline__ floatx4 mfma16x16x16(half4 a, half4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Raster row of every token of the chunk (-1 past the end of the sequence).
+template <int C>
+__device__ __forceinline__ void chunk_rows(int* sRow, int tok0, int T, int gh, int gw, int dir) {
   const int tid = threadIdx.x;
-  const int tok0 = n * C;
   const int L = min(C, T - tok0);
-  if (tid < C) sRow[tid] = tid < L ? scan_to_raster(tok0 + tid, T, gh, gw, dirs.get(b)) : -1;
-  __syncthreads();
+  if (tid < C) sRow[tid] = tid < L ? scan_to_raster(tok0 + tid, T, gh, gw, dir) : -1;
+}
 
-  // -- load k, gk (rows of dk) and v (rows of dv); padding rows are zero
-  for (int u = tid; u < C * (DK / 8); u += kThreads) {
-    const int r = u / (DK / 8), c8 = (u % (DK / 8)) * 8;
-    float g8[8];
-    half8 k8;
-    if (sRow[r] >= 0) {
-      const long row = ((long)b * T + sRow[r]) * H + h;
-      load8(gp + row * DK + c8, g8);
-      k8 = load8h(kp + row * DK + c8);
+// Token row t of a [B][T][H][D] tensor, this lane's 8*NKS dims
+// d = 32*ks + lk + c, in float (zero for padding rows).
+template <int D, int NKS, typename InT>
+__device__ __forceinline__ void load_row(const InT* p, long row, int lk, float* x) {
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (row >= 0) {
+      float y[8];
+      load8(p + row * D + 32 * ks + lk, y);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[8 * ks + c] = y[c];
     } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) { g8[c] = 0.f; k8[c] = (half_t)0.f; }
+      for (int c = 0; c < 8; ++c) x[8 * ks + c] = 0.f;
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) sG[r][c8 + c] = g8[c] * kLog2e;
-    *reinterpret_cast<half8*>(&sK[r][c8]) = k8;
   }
-  for (int u = tid; u < C * (DV / 8); u += kThreads) {
+}
+
+// V rows of the chunk, transposed into sVt[e][token] (half).
+template <int DV, int C, int VSTR, typename InT>
+__device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT, int H, int h,
+                                        half_t (*sVt)[VSTR]) {
+  for (int u = threadIdx.x; u < C * (DV / 8); u += kThreads) {
     const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
     half8 v8;
     if (sRow[r] >= 0) {
-      const long row = ((long)b * T + sRow[r]) * H + h;
-      v8 = load8h(vp + row * DV + c8);
+      v8 = load8h(vp + ((bT + sRow[r]) * H + h) * DV + c8);
     } else {
 #pragma unroll
       for (int c = 0; c < 8; ++c) v8[c] = (half_t)0.f;
     }
-    *reinterpret_cast<half8*>(&sV[r][c8]) = v8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sVt[c8 + c][r] = v8[c];
   }
+}
+
+// ===========================================================================
+// Phase 1: chunk summaries. One workgroup per (chunk n, head h, batch b).
+//   U^T[e][d] = sum_j V[j][e] K^[j][d],   K^[j] = k_j 2^(B - b_j)  (<= |k|)
+//   a[d]      = 2^(B[d])
+// Wave w owns the 16 tokens of sub-block w, one token per lane row, and
+// takes its cumulative decay with a DPP row scan plus the totals of the
+// earlier sub-blocks. K^ goes to LDS transposed (token-contiguous per key
+// dim), V likewise, so both operands of the token contraction are 8-byte
+// LDS reads; U is produced in 16x16 blocks on the matrix cores and stored
+// as half.
+// ===========================================================================
+template <int DK, int DV, int C, typename InT>
+__global__ __launch_bounds__(kThreads, 4) void summary_kernel(
+    const InT* __restrict__ kp, const InT* __restrict__ vp, const InT* __restrict__ gp,
+    half_t* __restrict__ Uws, float* __restrict__ Aws, int T, int H, int N, int gh, int gw,
+    DirPack dirs) {
+  constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
+  constexpr int VSTR = C + 8;    // halves, token-contiguous rows
+  constexpr int USTR = DK + 8;   // halves, staging rows of U^T
+  __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
+  __shared__ __attribute__((aligned(16))) half_t sKh[DK][VSTR];
+  __shared__ __attribute__((aligned(16))) half_t sU[DV][USTR];
+  __shared__ float sTot[NB][DK];
+  __shared__ int sRow[C];
+
+  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
+  chunk_rows<C>(sRow, n * C, T, gh, gw, dirs.get(b));
   __syncthreads();
 
-  // -- inclusive cumsum along tokens, one key dim per thread-column
-  const int d = tid % DK, seg = tid / DK;
-  float p[G::SEGLEN];
-  float run = 0.f;
-#pragma unroll
-  for (int i = 0; i < G::SEGLEN; ++i) {
-    run += sG[seg * G::SEGLEN + i][d];
-    p[i] = run;
+  const bool owner = wave < NB;
+  const int I = wave, t = 16 * I + lr;
+  float kf[NEL], sc[NEL];
+  if (owner) {
+    const long row = sRow[t] >= 0 ? ((long)b * T + sRow[t]) * H + h : -1;
+    load_row<DK, NKS>(kp, row, lk, kf);
+    load_row<DK, NKS>(gp, row, lk, sc);
   }
-  sTot[seg][d] = run;
-  __syncthreads();
-  float off = 0.f, tot = 0.f;
+  load_vt<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sVt);
+  if (owner) {
 #pragma unroll
-  for (int s = 0; s < G::NSEG; ++s) {
-    const float x = sTot[s][d];
-    if (s < seg) off += x;
-    tot += x;
-  }
-  // K^ transposed into [d][token]
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e] * kLog2e);
+    if (lr == 15) {
 #pragma unroll
-  for (int i = 0; i < G::SEGLEN; ++i) {
-    const int j = seg * G::SEGLEN + i;
-    sKt[d][j] = (half_t)((float)sK[j][d] * exp2f(tot - (off + p[i])));
-  }
-  const long bhn = ((long)b * H + h) * N + n;
-  if (seg == 0) Aws[bhn * DK + d] = exp2f(tot);
-  // V transposed into [e][token]
-  for (int u = tid; u < DV * (C / 8); u += kThreads) {
-    const int e = u % DV, j8 = (u / DV) * 8;
-    half8 x;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) x[c] = sV[j8 + c][e];
-    *reinterpret_cast<half8*>(&sVt[e][j8]) = x;
-  }
-  if constexpr (G::CP > C) {
-    for (int u = tid; u < (DK + DV) * (G::CP - C); u += kThreads) {
-      const int row = u / (G::CP - C), col = C + u % (G::CP - C);
-      if (row < DK) sKt[row][col] = (half_t)0.f;
-      else sVt[row - DK][col] = (half_t)0.f;
+      for (int e = 0; e < NEL; ++e) sTot[I][32 * (e / 8) + lk + (e % 8)] = sc[e];
     }
   }
   __syncthreads();
 
-  // -- U^T = V^T K^ on the matrix cores, 16x16 output blocks, K = tokens
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lk = 8 * (lane >> 4);
-  constexpr int NBD = DK / 16, NBLK = (DV / 16) * NBD;
-  float* Ub = Uws + bhn * (long)(DV * DK);
-  for (int blk = wave; blk < NBLK; blk += 4) {
-    const int E = blk / NBD, D = blk % NBD;
+  const long bhn = ((long)b * H + h) * N + n;
+  if (owner) {
+#pragma unroll
+    for (int e = 0; e < NEL; ++e) {
+      const int d = 32 * (e / 8) + lk + (e % 8);
+      float rest = sTot[I][d] - sc[e];  // B - b_t, summed over later tokens
+#pragma unroll
+      for (int J = 0; J < NB; ++J)
+        if (J > I) rest += sTot[J][d];
+      sKh[d][t] = (half_t)(kf[e] * fexp2(rest));
+    }
+  }
+  if (tid < DK) {
+    float B = 0.f;
+#pragma unroll
+    for (int J = 0; J < NB; ++J) B += sTot[J][tid];
+    Aws[bhn * DK + tid] = fexp2(B);
+  }
+  __syncthreads();
+
+  for (int blk = wave; blk < NE * ND; blk += 4) {
+    const int E = blk / ND, D = blk % ND;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < G::CP / 32; ++ks) {
-      const half8 a = *reinterpret_cast<const half8*>(&sVt[16 * E + lr][32 * ks + lk]);
-      const half8 bb = *reinterpret_cast<const half8*>(&sKt[16 * D + lr][32 * ks + lk]);
-      acc = mfma16x16x32(a, bb, acc);
+    for (int J = 0; J < NB; ++J) {
+      const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
+      const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][16 * J + 4 * lq]);
+      acc = mfma16x16x16(a, bb, acc);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ub[(16 * E + 4 * (lane >> 4) + r) * DK + 16 * D + lr] = acc[r];
+    for (int r = 0; r < 4; ++r) sU[16 * E + 4 * lq + r][16 * D + lr] = (half_t)acc[r];
+  }
+  __syncthreads();
+  half_t* Ub = Uws + bhn * (long)(DV * DK);
+  for (int u = tid; u < DV * (DK / 8); u += kThreads) {
+    const int e = u / (DK / 8), d8 = (u % (DK / 8)) * 8;
+    *reinterpret_cast<half8*>(Ub + e * DK + d8) = *reinterpret_cast<const half8*>(&sU[e][d8]);
   }
 }
 
@@ -166,36 +189,37 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
 // (batch, head); a wave covers 64 consecutive d of one value column e, so
 // every load and store is a coalesced row segment. Serial over chunks:
 //   S_0 = 0,  S_{n+1}[e][d] = a_n[d] * S_n[e][d] + U_n^T[e][d]
-// The state entering each chunk is stored (half, transposed [e][d]).
+// in fp32; the state entering each chunk is stored (half, transposed [e][d]).
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void scan_kernel(const float* __restrict__ Uws,
+__global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict__ Uws,
                                                         const float* __restrict__ Aws,
                                                         half_t* __restrict__ Sws, int N,
                                                         int DK, int DKDV) {
+  constexpr int PF = 16;  // chunks whose inputs are in flight at once
   const long bh = blockIdx.y;
   const int x = blockIdx.x * kThreads + threadIdx.x;
   const int d = x % DK;
-  const float* U = Uws + bh * N * (long)DKDV + x;
+  const half_t* U = Uws + bh * N * (long)DKDV + x;
   const float* A = Aws + bh * N * (long)DK + d;
   half_t* S = Sws + bh * N * (long)DKDV + x;
   float s = 0.f;
   int n = 0;
-  for (; n + 8 <= N; n += 8) {
-    float u[8], a[8];
+  for (; n + PF <= N; n += PF) {
+    float u[PF], a[PF];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u[i] = U[(long)(n + i) * DKDV];
+    for (int i = 0; i < PF; ++i) {
+      u[i] = (float)U[(long)(n + i) * DKDV];
       a[i] = A[(long)(n + i) * DK];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < PF; ++i) {
       S[(long)(n + i) * DKDV] = (half_t)s;
       s = a[i] * s + u[i];
     }
   }
   for (; n < N; ++n) {
     S[(long)n * DKDV] = (half_t)s;
-    s = A[(long)n * DK] * s + U[(long)n * DKDV];
+    s = A[(long)n * DK] * s + (float)U[(long)n * DKDV];
   }
 }
 
@@ -220,32 +244,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const float* __restrict_
 // 2^8 over a sub-block, fp32 operands up to 2^120, and beyond that (checked
 // per tile) sums every entry directly from 2^(s_i - s_j).
 // ===========================================================================
-__device__ __forceinline__ float row_scan16(float x) {
-  // inclusive prefix sum over the 16 lanes of each DPP row
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
-  return x;
-}
-
-__device__ __forceinline__ floatx4 mfma16x16x16(half4 a, half4 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-template <typename T>
-struct OutStage;
-template <>
-struct OutStage<half_t> {
-  typedef half_t type;
-};
-template <>
-struct OutStage<float> {
-  typedef float type;
-};
 
 template <int DK, int DV, int C, typename InT>
-__global__ __launch_bounds__(kThreads, 3) void output_kernel(
+__global__ __launch_bounds__(kThreads, 4) void output_kernel(
     const InT* __restrict__ qp, const InT* __restrict__ kp, const InT* __restrict__ vp,
     const InT* __restrict__ gp, const half_t* __restrict__ Sws, InT* __restrict__ op, int T,
     int H, int N, int gh, int gw, DirPack dirs) {
@@ -255,55 +256,39 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
   constexpr int VSTR = C + 8;   // halves, rows of V^T
   constexpr int OSTR = DV + 8;  // rows of the output staging tile
   constexpr float kHalfRange = 8.f, kF32Range = 120.f;  // log2 decay per sub-block
-  typedef typename OutStage<InT>::type OT;
-  __shared__ __attribute__((aligned(16))) half_t sKt[C][KSTR];
+  // K~ is dead once the score blocks are built; the output tile reuses it
+  constexpr int KO_BYTES = (C * KSTR * 2 > C * OSTR * (int)sizeof(InT)) ? C * KSTR * 2
+                                                                        : C * OSTR * (int)sizeof(InT);
+  __shared__ __attribute__((aligned(16))) char sKO[KO_BYTES];
   __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
   __shared__ __attribute__((aligned(16))) half_t sS[DV][KSTR];
-  __shared__ __attribute__((aligned(16))) OT sO[C][OSTR];
   __shared__ float sTot[NB][DK], sS7[NB][DK];
   __shared__ float sEb[NB][DK], sR1[NB][DK], sR2[NB][DK];
   __shared__ float sM[NPAIR > 0 ? NPAIR : 1][DK];
   __shared__ int sRow[C];
   __shared__ int sTier;
+  half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
+  InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
-  const int tok0 = n * C;
-  const int L = min(C, T - tok0);
-  if (tid < C) sRow[tid] = tid < L ? scan_to_raster(tok0 + tid, T, gh, gw, dirs.get(b)) : -1;
+  chunk_rows<C>(sRow, n * C, T, gh, gw, dirs.get(b));
   if (tid == 0) sTier = 0;
   __syncthreads();
 
   // -- this wave's token rows of q, k, gk in the operand layout
   const bool owner = wave < NB;
-  const int I = wave;
-  const int t = 16 * I + lr;
+  const int I = wave, t = 16 * I + lr;
   float qf[NEL], kf[NEL], sc[NEL];
   if (owner) {
-    const int row = sRow[t];
-    const long base = ((long)b * T + row) * H + h;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (row >= 0) {
-        const half8 q8 = load8h(qp + base * DK + 32 * ks + lk);
-        const half8 k8 = load8h(kp + base * DK + 32 * ks + lk);
-        float g8[8];
-        load8(gp + base * DK + 32 * ks + lk, g8);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          qf[8 * ks + c] = (float)q8[c];
-          kf[8 * ks + c] = (float)k8[c];
-          sc[8 * ks + c] = g8[c] * kLog2e;
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) qf[8 * ks + c] = kf[8 * ks + c] = sc[8 * ks + c] = 0.f;
-      }
-    }
+    const long row = sRow[t] >= 0 ? ((long)b * T + sRow[t]) * H + h : -1;
+    load_row<DK, NKS>(qp, row, lk, qf);
+    load_row<DK, NKS>(kp, row, lk, kf);
+    load_row<DK, NKS>(gp, row, lk, sc);
   }
-  // -- V rows transposed into V^T, and the entering state S^T, through LDS
+  // -- the entering state S^T and the chunk's V^T, through LDS
   {
     const long bhn = ((long)b * H + h) * N + n;
     const half_t* Sb = Sws + bhn * (long)(DV * DK);
@@ -311,24 +296,13 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
       const int e = u / (DK / 8), d8 = (u % (DK / 8)) * 8;
       *reinterpret_cast<half8*>(&sS[e][d8]) = load8h(Sb + e * DK + d8);
     }
-    for (int u = tid; u < C * (DV / 8); u += kThreads) {
-      const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
-      half8 v8;
-      if (sRow[r] >= 0) {
-        v8 = load8h(vp + (((long)b * T + sRow[r]) * H + h) * DV + c8);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v8[c] = (half_t)0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) sVt[c8 + c][r] = v8[c];
-    }
   }
+  load_vt<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sVt);
 
   // -- in-sub-block inclusive cumsum along tokens (DPP row scan)
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]);
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e] * kLog2e);
     if (lr == 15 || lr == 7) {
 #pragma unroll
       for (int e = 0; e < NEL; ++e) {
@@ -346,12 +320,12 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
     float beta = 0.f;
     for (int J = 0; J < I2; ++J) beta += sTot[J][d];
     const float tot = sTot[I2][d], s7 = sS7[I2][d];
-    sEb[I2][d] = exp2f(beta);
-    sR1[I2][d] = exp2f(-s7);
-    sR2[I2][d] = exp2f(s7 - tot);
+    sEb[I2][d] = fexp2(beta);
+    sR1[I2][d] = fexp2(-s7);
+    sR2[I2][d] = fexp2(s7 - tot);
     float acc = 0.f;  // log2 of m_{I2,J} for J = I2-1, I2-2, ...
     for (int J = I2 - 1; J >= 0; --J) {
-      sM[I2 * (I2 - 1) / 2 + J][d] = exp2f(acc);
+      sM[I2 * (I2 - 1) / 2 + J][d] = fexp2(acc);
       acc += sTot[J][d];
     }
     const float range = -tot;
@@ -368,8 +342,8 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
       for (int c = 0; c < 8; ++c) {
         const int e = 8 * ks + c;
         const float tot = sTot[I][32 * ks + lk + c];
-        qt[e] = qf[e] * exp2f(sc[e]);
-        kt[e] = kf[e] * exp2f(tot - sc[e]);
+        qt[e] = qf[e] * fexp2(sc[e]);
+        kt[e] = kf[e] * fexp2(tot - sc[e]);
         k8[c] = (half_t)kt[e];
       }
       *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = k8;
@@ -377,6 +351,8 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
   }
   __syncthreads();
 
+  half4 A[NB];
+  half8 qh[NKS];
   if (owner) {
     const int tier = sTier;
     // -- diagonal sub-block, transposed: acc[r] = A[i = lr][j = 4*lq + r]
@@ -409,14 +385,13 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
         for (int e = 0; e < NEL; ++e) {
           const float kj = __shfl(kf[e], (lane & 48) | j);
           const float sj = __shfl(sc[e], (lane & 48) | j);
-          part += qf[e] * kj * exp2f(sc[e] - sj);
+          part += qf[e] * kj * fexp2(sc[e] - sj);
         }
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
         if ((j >> 2) == lq) dacc[j & 3] = part;
       }
     }
-    half4 A[NB];
     half4 adiag;
 #pragma unroll
     for (int r = 0; r < 4; ++r) adiag[r] = (half_t)((4 * lq + r <= lr) ? dacc[r] : 0.f);
@@ -441,12 +416,15 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
         for (int r = 0; r < 4; ++r) A[J][r] = (half_t)acc[r];
       }
     }
-    // -- O_I = sum_{J<=I} A_IJ V_J + Q^_I S
-    half8 qh[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int c = 0; c < 8; ++c) qh[ks][c] = (half_t)(qt[8 * ks + c] * sEb[I][32 * ks + lk + c]);
+  }
+  __syncthreads();  // K~ is no longer read: its LDS becomes the output tile
+
+  // -- O_I = Q^_I S + sum_{J<=I} A_IJ V_J
+  if (owner) {
 #pragma unroll
     for (int E = 0; E < NE; ++E) {
       // one accumulation chain of a single product shape (16x16x16) per value
@@ -471,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 3) void output_kernel(
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (OT)acc[r];
+      for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (InT)acc[r];
     }
   }
   __syncthreads();
@@ -504,7 +482,7 @@ hipError_t summaries_t(const Problem& p, int b0, int nb, const DirPack& dirs, co
   hipLaunchKernelGGL((summary_kernel<DK, DV, C, InT>), grid, dim3(kThreads), 0, s,
                      static_cast<const InT*>(k) + tok * DK, static_cast<const InT*>(v) + tok * DV,
                      static_cast<const InT*>(gk) + tok * DK,
-                     reinterpret_cast<float*>(ws + w.off_U) + bhn * DK * DV,
+                     reinterpret_cast<half_t*>(ws + w.off_U) + bhn * DK * DV,
                      reinterpret_cast<float*>(ws + w.off_a) + bhn * DK, p.T, p.H, p.N, p.gh,
                      p.gw, dirs);
   return hipGetLastError();
@@ -554,7 +532,7 @@ WsLayout workspace_layout(const Problem& p) {
   const size_t units = (size_t)p.B * p.H * p.N;
   WsLayout w;
   w.off_U = 0;
-  w.off_a = up(units * p.dk * p.dv * sizeof(float));
+  w.off_a = up(units * p.dk * p.dv * sizeof(half_t));
   w.off_S = w.off_a + up(units * p.dk * sizeof(float));
   w.total = w.off_S + up(units * p.dk * p.dv * sizeof(half_t));
   return w;
@@ -572,7 +550,7 @@ hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, hipStream_t s
   const int dkdv = p.dk * p.dv;
   dim3 grid(dkdv / kThreads, nb * p.H);
   hipLaunchKernelGGL(scan_kernel, grid, dim3(kThreads), 0, s,
-                     reinterpret_cast<const float*>(ws + w.off_U) + bhn * dkdv,
+                     reinterpret_cast<const half_t*>(ws + w.off_U) + bhn * dkdv,
                      reinterpret_cast<const float*>(ws + w.off_a) + bhn * p.dk,
                      reinterpret_cast<half_t*>(ws + w.off_S) + bhn * dkdv, p.N, p.dk, dkdv);
   return hipGetLastError();

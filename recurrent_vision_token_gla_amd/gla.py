@@ -185,11 +185,11 @@ def chunk_outputs(q, k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspac
 
 
 def workspace_views(workspace: torch.Tensor, B, H, grid_h, grid_w, dk, dv, chunk=64):
-    """Views of U [B,H,N,dv,dk] f32, a [B,H,N,dk] f32, S [B,H,N,dv,dk] f16."""
+    """Views of U [B,H,N,dv,dk] f16, a [B,H,N,dk] f32, S [B,H,N,dv,dk] f16."""
     off_U, off_a, off_S, _ = workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk)
     N = -(-(grid_h * grid_w) // chunk)
     n_us = B * H * N * dk * dv
-    U = workspace[off_U:off_U + 4 * n_us].view(torch.float32).view(B, H, N, dv, dk)
+    U = workspace[off_U:off_U + 2 * n_us].view(torch.float16).view(B, H, N, dv, dk)
     a = workspace[off_a:off_a + 4 * B * H * N * dk].view(torch.float32).view(B, H, N, dk)
     S = workspace[off_S:off_S + 2 * n_us].view(torch.float16).view(B, H, N, dv, dk)
     return U, a, S

@@ -47,11 +47,11 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # U (f32) + a (f32) + S (f16), each padded to 256 bytes
+    # U (f16) + a (f32) + S (f16), each padded to 256 bytes
     B, H, gh, gw, dk, dv, C = 1, 6, 40, 40, 64, 64, 64
     N = 25
     units = B * H * N
-    expect = units * dk * dv * 4 + units * dk * 4 + units * dk * dv * 2
+    expect = units * dk * dv * 2 + units * dk * 4 + units * dk * dv * 2
     assert gla.workspace_bytes(B, H, gh, gw, dk, dv, C) == expect
     assert gla.workspace_bytes(0, H, gh, gw, dk, dv, C) == 0
     assert gla.workspace_bytes(1, 1, 5, 7, 32, 32, 16) > 0
