@@ -105,18 +105,21 @@ __device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT,
 // as half.
 // ===========================================================================
 template <int DK, int DV, int C, typename InT>
-__global__ __launch_bounds__(kThreads, 4) void summary_kernel(
+__global__ __launch_bounds__(kThreads, 8) void summary_kernel(
     const InT* __restrict__ kp, const InT* __restrict__ vp, const InT* __restrict__ gp,
     half_t* __restrict__ Uws, float* __restrict__ Aws, int T, int H, int N, int gh, int gw,
     DirPack dirs) {
   constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
   constexpr int VSTR = C + 8;    // halves, token-contiguous rows
   constexpr int USTR = DK + 8;   // halves, staging rows of U^T
+  // the U^T staging tile reuses K^T's LDS once the products have read it
+  constexpr int KU_BYTES = (DK * VSTR > DV * USTR ? DK * VSTR : DV * USTR) * 2;
   __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
-  __shared__ __attribute__((aligned(16))) half_t sKh[DK][VSTR];
-  __shared__ __attribute__((aligned(16))) half_t sU[DV][USTR];
+  __shared__ __attribute__((aligned(16))) char sKU[KU_BYTES];
   __shared__ float sTot[NB][DK];
   __shared__ int sRow[C];
+  half_t (*sKh)[VSTR] = reinterpret_cast<half_t (*)[VSTR]>(sKU);
+  half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sKU);
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -164,17 +167,31 @@ __global__ __launch_bounds__(kThreads, 4) void summary_kernel(
   }
   __syncthreads();
 
-  for (int blk = wave; blk < NE * ND; blk += 4) {
-    const int E = blk / ND, D = blk % ND;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NBLK = NE * ND, BPW = (NBLK + 3) / 4;  // output blocks per wave
+  floatx4 acc[BPW];
 #pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
-      const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][16 * J + 4 * lq]);
-      acc = mfma16x16x16(a, bb, acc);
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + 4 * i;
+    acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (blk < NBLK) {
+      const int E = blk / ND, D = blk % ND;
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
+        const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][16 * J + 4 * lq]);
+        acc[i] = mfma16x16x16(a, bb, acc[i]);
+      }
     }
+  }
+  __syncthreads();  // K^T is no longer read
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sU[16 * E + 4 * lq + r][16 * D + lr] = (half_t)acc[r];
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + 4 * i;
+    if (blk < NBLK) {
+      const int E = blk / ND, D = blk % ND;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sU[16 * E + 4 * lq + r][16 * D + lr] = (half_t)acc[i][r];
+    }
   }
   __syncthreads();
   half_t* Ub = Uws + bhn * (long)(DV * DK);
@@ -195,31 +212,43 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
                                                         const float* __restrict__ Aws,
                                                         half_t* __restrict__ Sws, int N,
                                                         int DK, int DKDV) {
-  constexpr int PF = 16;  // chunks whose inputs are in flight at once
+  constexpr int PF = 8;  // chunks per pipeline stage; two stages in flight
   const long bh = blockIdx.y;
   const int x = blockIdx.x * kThreads + threadIdx.x;
   const int d = x % DK;
   const half_t* U = Uws + bh * N * (long)DKDV + x;
   const float* A = Aws + bh * N * (long)DK + d;
   half_t* S = Sws + bh * N * (long)DKDV + x;
+  // loads use indices clamped to the last chunk, so they are always in
+  // bounds; values past the end are never consumed
+  auto fetch = [&](int n0, float (&u)[PF], float (&a)[PF]) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const long m = min(n0 + i, N - 1);
+      u[i] = (float)U[m * DKDV];
+      a[i] = A[m * DK];
+    }
+  };
   float s = 0.f;
-  int n = 0;
-  for (; n + PF <= N; n += PF) {
-    float u[PF], a[PF];
+  float u0[PF], a0[PF], u1[PF], a1[PF];
+  fetch(0, u0, a0);
+  for (int n = 0; n < N; n += 2 * PF) {
+    fetch(n + PF, u1, a1);
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      u[i] = (float)U[(long)(n + i) * DKDV];
-      a[i] = A[(long)(n + i) * DK];
+      if (n + i < N) {
+        S[(long)(n + i) * DKDV] = (half_t)s;
+        s = a0[i] * s + u0[i];
+      }
     }
+    fetch(n + 2 * PF, u0, a0);
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      S[(long)(n + i) * DKDV] = (half_t)s;
-      s = a[i] * s + u[i];
+      if (n + PF + i < N) {
+        S[(long)(n + PF + i) * DKDV] = (half_t)s;
+        s = a1[i] * s + u1[i];
+      }
     }
-  }
-  for (; n < N; ++n) {
-    S[(long)n * DKDV] = (half_t)s;
-    s = A[(long)n * DK] * s + (float)U[(long)n * DKDV];
   }
 }
 
