@@ -138,29 +138,48 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
         b.synchronize()
         lat.append(a.elapsed_time(b) * 1e3)
 
-    # per-phase kernel durations: each phase alone, back to back, events on
-    # the stream it is launched on (torch's current stream)
+    # per-phase kernel durations: each phase alone, `timing_reps` launches
+    # captured back to back in one graph (no host gaps), timed with events on
+    # the stream the kernels are launched on
     c0 = calls[0]
-    phases = {
-        "summaries": lambda: gla.chunk_summaries(c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
-                                                 c0["dirs"], w.chunk, workspace=ws),
-        "scan": lambda: gla.state_scan(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, ws),
-        "outputs": lambda: gla.chunk_outputs(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h,
-                                             w.grid_w, c0["dirs"], w.chunk, workspace=ws,
-                                             out=c0["out"]),
-    }
+
+    def phases(s):
+        return {
+            "summaries": lambda: gla.chunk_summaries(c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
+                                                     c0["dirs"], w.chunk, workspace=ws, stream=s),
+            "scan": lambda: gla.state_scan(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, ws,
+                                           stream=s),
+            "outputs": lambda: gla.chunk_outputs(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h,
+                                                 w.grid_w, c0["dirs"], w.chunk, workspace=ws,
+                                                 out=c0["out"], stream=s),
+        }
+
     phase_us = {}
-    for name, fn in phases.items():
-        fn()
+    for name in ("summaries", "scan", "outputs"):
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        fn = phases(s)[name]
+        pg = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            fn()
+            with torch.cuda.graph(pg, stream=s):
+                for _ in range(timing_reps):
+                    fn()
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        pg.replay()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(timing_reps):
-            fn()
+        for _ in range(3):
+            pg.replay()
         b.record()
         b.synchronize()
-        phase_us[name] = a.elapsed_time(b) * 1e3 / timing_reps
+        phase_us[name] = a.elapsed_time(b) * 1e3 / (3 * timing_reps)
+    # the full step ran last on the workspace: re-run it so outputs are current
+    run()
+    torch.cuda.synchronize()
     return dict(calls=calls, ms_per_step=ms_per_step, wall_s=wall, lat_us=lat,
                 phase_us=phase_us, ws=ws)
 
