@@ -19,7 +19,7 @@ Per chunk n of one (batch, head), with local token index i = 0..L-1:
     b_i   = sum_{r <= i} g_r                 cumulative log-decay (dk-vector)
     B_n   = b_{L-1},  a_n = exp(B_n)          total decay of the chunk
     U_n   = sum_j diag(exp(B_n - b_j)) k_j^T v_j           chunk summary
-    S_0   = 0,  S_{n+1} = diag(a_n) S_n + U_n              boundary scan
+    S_0   = 0 (or a carried state),  S_{n+1} = diag(a_n) S_n + U_n   scan
     A_ij  = sum_d q_i[d] k_j[d] exp(b_i[d] - b_j[d]),  j <= i, else 0
     o_i   = sum_j A_ij v_j + (q_i * exp(b_i)) S_n          output
 A last chunk shorter than C is simply shorter (L < C).
@@ -29,11 +29,13 @@ from __future__ import annotations
 import numpy as np
 
 
-def chunkwise(q, k, v, g, chunk: int, return_states: bool = False):
+def chunkwise(q, k, v, g, chunk: int, return_states: bool = False, s0=None):
     """Scan-ordered [B, T, H, D] inputs -> scan-ordered o (float64).
 
-    With return_states, also returns U [B, H, N, dk, dv], a [B, H, N, dk] and
-    the states entering every chunk S [B, H, N, dk, dv].
+    s0 [B, H, dk, dv] is the state before the first token (None for zero).
+    With return_states, also returns U [B, H, N, dk, dv], a [B, H, N, dk],
+    the states entering every chunk S [B, H, N, dk, dv] and the state after
+    the last chunk [B, H, dk, dv].
     """
     q, k, v, g = (np.asarray(x, np.float64) for x in (q, k, v, g))
     B, T, H, dk = q.shape
@@ -58,7 +60,7 @@ def chunkwise(q, k, v, g, chunk: int, return_states: bool = False):
         U[:, :, n] = np.einsum("bhjd,bhje->bhde", kdec, vh[:, :, sl])
 
     # boundary-state scan, sequential over chunks
-    S = np.zeros((B, H, dk, dv))
+    S = np.zeros((B, H, dk, dv)) if s0 is None else np.array(s0, np.float64)
     for n in range(N):
         S_in[:, :, n] = S
         S = a[:, :, n][..., None] * S + U[:, :, n]
@@ -78,5 +80,5 @@ def chunkwise(q, k, v, g, chunk: int, return_states: bool = False):
                             S_in[:, :, n])
         o[:, sl] = np.transpose(intra + readout, (0, 2, 1, 3))
     if return_states:
-        return o, U, a, S_in
+        return o, U, a, S_in, S
     return o

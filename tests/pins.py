@@ -6,6 +6,8 @@ checks run on the oracle (they must pass) and on copies with planted mistakes
 
   scan   -- callable (grid_h, grid_w, direction) -> permutation array
   rec    -- callable (q, k, v, g) -> o, scan-ordered [B, T, H, D] float64
+  rec_state -- callable (q, k, v, g, s0) -> (o, S_T): the carried-state
+            form, s0 and S_T [B, H, dk, dv]
   chunked-- callable (q, k, v, g, chunk) -> o, same convention
 
 What pins what:
@@ -20,7 +22,11 @@ What pins what:
   * invariants: linear in v, value columns independent, (batch, head) slices
     independent, reversed direction equals reversing the token sequence,
     top->bottom equals left->right on the transposed grid;
-  * the scan-order permutation against its arithmetic closed form.
+  * the scan-order permutation against its arithmetic closed form;
+  * carried state: hand-derived fixtures, the brute-force closed form with
+    the decayed initial state, no decay (S_0 + K^T V), a zero S_0 equals the
+    stateless forward, and splitting a sequence anywhere and carrying the
+    state across the cut changes nothing.
 """
 from __future__ import annotations
 
@@ -242,6 +248,79 @@ def check_chunk_independence(rec, chunked, seed=8):
             o = chunked(q, k, v, g, C)
             err = np.max(np.abs(o - ref)) / np.max(np.abs(ref))
             assert err <= 1e-12, (T, C, err)
+
+
+def brute_force_state(q, k, v, g, s0):
+    """The recurrence unrolled from S_0:
+    o_t = q_t diag(exp(G_t)) S_0 + sum_{s<=t} (q_t . k_s exp(G_t - G_s)) v_s,
+    S_T = diag(exp(G_{T-1})) S_0 + sum_s diag(exp(G_{T-1} - G_s)) k_s^T v_s."""
+    o = brute_force(q, k, v, g)
+    G = np.cumsum(g, axis=1)
+    B, T, H, dk = q.shape
+    for t in range(T):
+        o[:, t] += np.einsum("bhd,bhde->bhe", q[:, t] * np.exp(G[:, t]), s0)
+    w = np.exp(G[:, -1:] - G)                               # [B, T, H, dk]
+    sT = np.exp(G[:, -1])[..., None] * s0 + np.einsum("bthd,bthe->bhde", k * w, v)
+    return o, sT
+
+
+def check_golden_state(rec_state):
+    for case in load_golden("state_cases.json")["cases"]:
+        arr = lambda key: np.asarray(case[key], np.float64)[None, :, None, :]
+        s0 = np.asarray(case["s0"], np.float64)[None, None]
+        o, sT = rec_state(arr("q"), arr("k"), arr("v"), arr("g"), s0)
+        np.testing.assert_allclose(o[0, :, 0, :], case["o"], rtol=1e-12, atol=1e-12,
+                                   err_msg=case["name"])
+        np.testing.assert_allclose(sT[0, 0], case["s_final"], rtol=1e-12, atol=1e-12,
+                                   err_msg=case["name"])
+
+
+def check_state_brute_force(rec_state, seed=20):
+    rng = np.random.default_rng(seed)
+    for (B, T, H, dk, dv) in [(1, 1, 1, 1, 1), (2, 6, 2, 3, 3), (1, 9, 2, 4, 2)]:
+        q, k, v, g = rand_inputs(rng, B, T, H, dk, dv)
+        s0 = rng.standard_normal((B, H, dk, dv))
+        ro, rs = brute_force_state(q, k, v, g, s0)
+        o, sT = rec_state(q, k, v, g, s0)
+        assert np.max(np.abs(o - ro)) <= 1e-10 * np.max(np.abs(ro)), (B, T, H, dk, dv)
+        assert np.max(np.abs(sT - rs)) <= 1e-10 * np.max(np.abs(rs)), (B, T, H, dk, dv)
+
+
+def check_state_no_decay(rec_state, seed=21):
+    rng = np.random.default_rng(seed)
+    q, k, v, _ = rand_inputs(rng, 1, 7, 1, 3, 3)
+    s0 = rng.standard_normal((1, 1, 3, 3))
+    o, sT = rec_state(q, k, v, np.zeros_like(q), s0)
+    Q, K, V = q[0, :, 0], k[0, :, 0], v[0, :, 0]
+    np.testing.assert_allclose(o[0, :, 0], Q @ s0[0, 0] + np.tril(Q @ K.T) @ V,
+                               rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(sT[0, 0], s0[0, 0] + K.T @ V, rtol=1e-11, atol=1e-11)
+
+
+def check_state_split(rec_state, seed=22):
+    """Running [x1; x2] from S_0 equals running x1 from S_0, then x2 from the
+    state x1 hands back: same outputs, same final state."""
+    rng = np.random.default_rng(seed)
+    T = 11
+    q, k, v, g = rand_inputs(rng, 2, T, 2, 3, 4)
+    s0 = rng.standard_normal((2, 2, 3, 4))
+    o, sT = rec_state(q, k, v, g, s0)
+    for cut in (1, 4, 10):
+        o1, s1 = rec_state(q[:, :cut], k[:, :cut], v[:, :cut], g[:, :cut], s0)
+        o2, s2 = rec_state(q[:, cut:], k[:, cut:], v[:, cut:], g[:, cut:], s1)
+        np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), o, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(s2, sT, rtol=1e-11, atol=1e-11)
+
+
+def check_state_zero_is_stateless(rec_state, rec, seed=23):
+    rng = np.random.default_rng(seed)
+    q, k, v, g = rand_inputs(rng, 2, 8, 2, 4, 3)
+    o, _ = rec_state(q, k, v, g, np.zeros((2, 2, 4, 3)))
+    np.testing.assert_allclose(o, rec(q, k, v, g), rtol=1e-12, atol=1e-12)
+
+
+ALL_STATE_CHECKS = [check_golden_state, check_state_brute_force, check_state_no_decay,
+                    check_state_split]
 
 
 ALL_REC_CHECKS = [check_golden_recurrence, check_brute_force,

@@ -99,7 +99,7 @@ def test_phase_intermediates_match_chunked_model():
     torch.cuda.synchronize()
     U, a, S = (x.double().cpu().numpy() for x in gla.workspace_views(ws, B, H, gh, gw, dk, dv, C))
     s = lambda x: oracle.to_scan(x, gh, gw, dirs)
-    _, U_ref, a_ref, S_ref = oracle.chunkwise(s(q), s(k), s(v), s(g), C, return_states=True)
+    _, U_ref, a_ref, S_ref, _ = oracle.chunkwise(s(q), s(k), s(v), s(g), C, return_states=True)
     say(f"U err {rel_err(U, U_ref.swapaxes(-1, -2)):.2e}  a err {rel_err(a, a_ref):.2e}  "
         f"S err {rel_err(S, S_ref.swapaxes(-1, -2)):.2e}")
     assert rel_err(U, U_ref.swapaxes(-1, -2)) <= 2e-3

@@ -170,3 +170,43 @@ def test_chunked_mutant_is_caught(mistake):
 def test_unmutated_chunked_copy_passes():
     chunked = lambda q, k, v, g, C: _chunked_generic(q, k, v, g, C, None)
     pins.check_chunk_independence(oracle.recurrence_c, chunked)
+
+
+def _rec_state_generic(q, k, v, g, s0, mistake=None):
+    """The carried-state recurrence with one planted mistake."""
+    q, k, v, g, s0 = (np.asarray(x, np.float64) for x in (q, k, v, g, s0))
+    B, T, H, dk = q.shape
+    S = np.zeros_like(s0) if mistake == "s0_ignored" else s0.copy()
+    if mistake == "s0_transposed":
+        S = np.swapaxes(s0, -1, -2).copy()
+    o = np.zeros(v.shape)
+    prev = S
+    for t in range(T):
+        a = np.exp(g[:, t])[..., None]
+        if mistake == "s0_not_decayed" and t == 0:
+            a = 1.0
+        prev = S
+        S = a * S + k[:, t][..., None] * v[:, t][:, :, None, :]
+        o[:, t] = np.einsum("bhd,bhde->bhe", q[:, t], S)
+    if mistake == "final_before_last_token":
+        return o, prev
+    if mistake == "final_decayed_twice":
+        return o, np.exp(g[:, -1])[..., None] * S
+    return o, S
+
+
+STATE_MUTANTS = ["s0_ignored", "s0_transposed", "s0_not_decayed", "final_before_last_token",
+                 "final_decayed_twice"]
+
+
+@pytest.mark.parametrize("mistake", STATE_MUTANTS)
+def test_state_mutant_is_caught(mistake):
+    rec_state = lambda q, k, v, g, s0: _rec_state_generic(q, k, v, g, s0, mistake)
+    checks = [(c.__name__, lambda c=c: c(rec_state)) for c in pins.ALL_STATE_CHECKS]
+    assert _failures(checks), f"no pin caught state mutant {mistake}"
+
+
+def test_unmutated_state_copy_passes():
+    rec_state = lambda q, k, v, g, s0: _rec_state_generic(q, k, v, g, s0, None)
+    checks = [(c.__name__, lambda c=c: c(rec_state)) for c in pins.ALL_STATE_CHECKS]
+    assert _failures(checks) == []

@@ -32,6 +32,36 @@ def test_recurrence_pins(rec, check):
     check(rec)
 
 
+@pytest.fixture(scope="module", params=["c", "numpy"])
+def rec_state(request):
+    f = oracle.recurrence_c if request.param == "c" else oracle.recurrence_numpy
+    return lambda q, k, v, g, s0: f(q, k, v, g, s0=s0, return_state=True)
+
+
+@pytest.mark.parametrize("check", pins.ALL_STATE_CHECKS, ids=lambda f: f.__name__)
+def test_carried_state_pins(rec_state, check):
+    check(rec_state)
+
+
+def test_zero_state_is_stateless(rec_state, rec):
+    pins.check_state_zero_is_stateless(rec_state, rec)
+
+
+def test_chunked_model_carries_state():
+    """The chunked schedule started from S_0 reproduces the recurrence from
+    S_0, outputs and final state, for any chunk size."""
+    rng = np.random.default_rng(24)
+    for T in (5, 64, 70):
+        q, k, v, g = pins.rand_inputs(rng, 2, T, 2, 4, 3)
+        s0 = rng.standard_normal((2, 2, 4, 3))
+        ref_o, ref_s = oracle.recurrence_c(q, k, v, g, s0=s0, return_state=True)
+        for C in (1, 4, 16, 64):
+            o, _, _, S_in, sT = oracle.chunkwise(q, k, v, g, C, return_states=True, s0=s0)
+            assert np.max(np.abs(o - ref_o)) <= 1e-12 * np.max(np.abs(ref_o)), (T, C)
+            assert np.max(np.abs(sT - ref_s)) <= 1e-12 * np.max(np.abs(ref_s)), (T, C)
+            np.testing.assert_allclose(S_in[:, :, 0], s0, rtol=0, atol=0)
+
+
 def test_golden_forward_all_directions(rec):
     pins.check_golden_forward(oracle.scan_order, rec)
 
@@ -57,7 +87,7 @@ def test_chunked_model_states():
     rng = np.random.default_rng(12)
     q, k, v, g = pins.rand_inputs(rng, 1, 50, 1, 3, 2)
     C = 16
-    _, U, a, S_in = oracle.chunkwise(q, k, v, g, C, return_states=True)
+    _, U, a, S_in, _ = oracle.chunkwise(q, k, v, g, C, return_states=True)
     S = np.zeros((3, 2))
     for t in range(50):
         if t % C == 0:
