@@ -82,9 +82,9 @@ size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk,
 
 /* Byte offsets, within the workspace, of the three intermediate arrays, so
  * that callers (tests) can inspect them after the phase calls below:
- *   U : half  [B][H][N][dv][dk]   chunk summaries, stored transposed (row e)
+ *   U : half  [B][H][N][dk][dv]   chunk summaries
  *   a : float [B][H][N][dk]       per-chunk total decay exp(sum of gk)
- *   S : half  [B][H][N][dv][dk]   state entering each chunk, transposed
+ *   S : half  [B][H][N][dk][dv]   state entering each chunk
  * with N = ceil(T / chunk). Returns GLA_OK or GLA_E_ARG/GLA_E_UNSUPPORTED. */
 int gla_workspace_layout(int B, int H, int grid_h, int grid_w, int dk, int dv,
                          int chunk, size_t* off_U, size_t* off_a,
@@ -99,6 +99,24 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* gk,
             const int32_t* dir, int chunk, int dtype, void* workspace,
             size_t workspace_bytes, void* stream);
 
+/* The forward with a carried state (ai.info summary of GTR, "Future
+ * Directions": carrying the recurrent state across frames; the deployed
+ * operator fixes it at zero, "Methodology in Plain English"). Same as
+ * gla_fwd, except that the state before the first scan token is s0 instead
+ * of zero, and the state after the last scan token, S_T, is written to
+ * s_final:
+ *   s0      : const float [B][H][dk][dv], or NULL for a zero state;
+ *   s_final : float [B][H][dk][dv], or NULL to skip the hand-back.
+ * Both are in the scan's own frame (no spatial order); 16-byte aligned
+ * device memory owned by the caller. s_final may be the same buffer as s0
+ * (the state is then updated in place) but must not otherwise overlap s0,
+ * the workspace or any tensor of the call. With both NULL this is gla_fwd. */
+int gla_fwd_state(const void* q, const void* k, const void* v, const void* gk,
+                  void* o, int B, int H, int grid_h, int grid_w, int dk, int dv,
+                  const int32_t* dir, int chunk, int dtype, const float* s0,
+                  float* s_final, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* Phase 1 alone: chunk summaries into the workspace's U and a (for every
  * (chunk, head) in parallel; ai.info summary of GTR, "Methodology in Plain
  * English"). U_n = sum_j diag(exp(B_n - b_j)) k_j^T v_j with b_j the
@@ -109,13 +127,15 @@ int gla_chunk_summaries(const void* k, const void* v, const void* gk, int B,
                         const int32_t* dir, int chunk, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Phase 2 alone: boundary-state scan over the chunk axis, S_0 = 0,
- * S_{n+1} = diag(a_n) S_n + U_n, from the workspace's U and a into its S
- * (project page, "A Kernel That Makes Recurrence Fast": only the boundary
- * states are carried sequentially). */
+/* Phase 2 alone: boundary-state scan over the chunk axis, S_0 = s0 (zero if
+ * s0 is NULL), S_{n+1} = diag(a_n) S_n + U_n, from the workspace's U and a
+ * into its S (project page, "A Kernel That Makes Recurrence Fast": only the
+ * boundary states are carried sequentially). If s_final is not NULL, the
+ * state after the last chunk is written there. s0 and s_final as in
+ * gla_fwd_state. */
 int gla_state_scan(int B, int H, int grid_h, int grid_w, int dk, int dv,
-                   int chunk, void* workspace, size_t workspace_bytes,
-                   void* stream);
+                   int chunk, const float* s0, float* s_final, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Phase 3 alone: every chunk's outputs from its tokens and the workspace's
  * S: o_i = sum_{j<=i} A_ij v_j + (q_i * exp(b_i)) S_n with

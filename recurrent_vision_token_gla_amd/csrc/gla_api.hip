@@ -73,7 +73,7 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
 
 extern "C" {
 
-int gla_abi_version(void) { return 1; }
+int gla_abi_version(void) { return 2; }
 
 size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv,
                                int chunk) {
@@ -123,16 +123,20 @@ int gla_chunk_summaries(const void* k, const void* v, const void* gk, int B, int
 }
 
 int gla_state_scan(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   const float* s0, float* s_final, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   gla::Problem p;
   bool empty;
   GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, GLA_F16, &p, &empty));
   if (empty) return GLA_OK;
+  if (s0) GLA_TRY(check_tensor(s0));
+  if (s_final) GLA_TRY(check_tensor(s_final));
   GLA_TRY(check_ws(p, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
     const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
-    const hipError_t e = gla::launch_scan(p, b0, nb, static_cast<char*>(workspace), s);
+    const hipError_t e =
+        gla::launch_scan(p, b0, nb, static_cast<char*>(workspace), s0, s_final, s);
     if (e != hipSuccess) return fail_hip(e, "boundary scan launch");
   }
   return GLA_OK;
@@ -164,9 +168,10 @@ int gla_chunk_outputs(const void* q, const void* k, const void* v, const void* g
   return GLA_OK;
 }
 
-int gla_fwd(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
-            int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
-            void* workspace, size_t workspace_bytes, void* stream) {
+int gla_fwd_state(const void* q, const void* k, const void* v, const void* gk, void* o, int B,
+                  int H, int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk,
+                  int dtype, const float* s0, float* s_final, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   gla::Problem p;
   bool empty;
   GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
@@ -178,14 +183,27 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* gk, void* o
   GLA_TRY(check_tensor(gk));
   GLA_TRY(check_tensor(o));
   if (o == q || o == k || o == v || o == gk) return GLA_E_ARG;
+  if (s0) GLA_TRY(check_tensor(s0));
+  if (s_final) {
+    GLA_TRY(check_tensor(s_final));
+    const void* sf = s_final;
+    if (sf == q || sf == k || sf == v || sf == gk || sf == o || sf == workspace) return GLA_E_ARG;
+  }
   GLA_TRY(check_dirs(dir, B));
   GLA_TRY(check_ws(p, workspace, workspace_bytes));
   GLA_TRY(gla_chunk_summaries(k, v, gk, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
                               workspace, workspace_bytes, stream));
-  GLA_TRY(gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace, workspace_bytes,
-                         stream));
+  GLA_TRY(gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, s0, s_final, workspace,
+                         workspace_bytes, stream));
   return gla_chunk_outputs(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
                            workspace, workspace_bytes, stream);
+}
+
+int gla_fwd(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
+            int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  return gla_fwd_state(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, nullptr,
+                       nullptr, workspace, workspace_bytes, stream);
 }
 
 int gla_scan_perm(int32_t* perm_dev, int grid_h, int grid_w, int dir, void* stream) {

@@ -95,14 +95,14 @@ __device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT,
 
 // ===========================================================================
 // Phase 1: chunk summaries. One workgroup per (chunk n, head h, batch b).
-//   U^T[e][d] = sum_j V[j][e] K^[j][d],   K^[j] = k_j 2^(B - b_j)  (<= |k|)
+//   U[d][e] = sum_j K^[j][d] V[j][e],     K^[j] = k_j 2^(B - b_j)  (<= |k|)
 //   a[d]      = 2^(B[d])
 // Wave w owns the 16 tokens of sub-block w, one token per lane row, and
 // takes its cumulative decay with a DPP row scan plus the totals of the
 // earlier sub-blocks. K^ goes to LDS transposed (token-contiguous per key
 // dim), V likewise, so both operands of the token contraction are 8-byte
-// LDS reads; U is produced in 16x16 blocks on the matrix cores and stored
-// as half.
+// LDS reads; U is produced (as U^T) in 16x16 blocks on the matrix cores,
+// staged through LDS as rows of key dims and stored as half [dk][dv].
 // ===========================================================================
 template <int DK, int DV, int C, typename InT>
 __global__ __launch_bounds__(kThreads, 8) void summary_kernel(
@@ -111,9 +111,9 @@ __global__ __launch_bounds__(kThreads, 8) void summary_kernel(
     DirPack dirs) {
   constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
   constexpr int VSTR = C + 8;    // halves, token-contiguous rows
-  constexpr int USTR = DK + 8;   // halves, staging rows of U^T
-  // the U^T staging tile reuses K^T's LDS once the products have read it
-  constexpr int KU_BYTES = (DK * VSTR > DV * USTR ? DK * VSTR : DV * USTR) * 2;
+  constexpr int USTR = DV + 8;   // halves, staging rows of U (one row per key dim)
+  // the U staging tile reuses K^T's LDS once the products have read it
+  constexpr int KU_BYTES = (VSTR > USTR ? VSTR : USTR) * DK * 2;
   __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
   __shared__ __attribute__((aligned(16))) char sKU[KU_BYTES];
   __shared__ float sTot[NB][DK];
@@ -189,64 +189,144 @@ __global__ __launch_bounds__(kThreads, 8) void summary_kernel(
     const int blk = wave + 4 * i;
     if (blk < NBLK) {
       const int E = blk / ND, D = blk % ND;
+      half4 h;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sU[16 * E + 4 * lq + r][16 * D + lr] = (half_t)acc[i][r];
+      for (int r = 0; r < 4; ++r) h[r] = (half_t)acc[i][r];
+      *reinterpret_cast<half4*>(&sU[16 * D + lr][16 * E + 4 * lq]) = h;
     }
   }
   __syncthreads();
   half_t* Ub = Uws + bhn * (long)(DV * DK);
-  for (int u = tid; u < DV * (DK / 8); u += kThreads) {
-    const int e = u / (DK / 8), d8 = (u % (DK / 8)) * 8;
-    *reinterpret_cast<half8*>(Ub + e * DK + d8) = *reinterpret_cast<const half8*>(&sU[e][d8]);
+  for (int u = tid; u < DK * (DV / 8); u += kThreads) {
+    const int d = u / (DV / 8), e8 = (u % (DV / 8)) * 8;
+    *reinterpret_cast<half8*>(Ub + d * DV + e8) = *reinterpret_cast<const half8*>(&sU[d][e8]);
   }
 }
 
 // ===========================================================================
-// Phase 2: boundary-state scan. One thread per state element (e, d) of one
-// (batch, head); a wave covers 64 consecutive d of one value column e, so
-// every load and store is a coalesced row segment. Serial over chunks:
-//   S_0 = 0,  S_{n+1}[e][d] = a_n[d] * S_n[e][d] + U_n^T[e][d]
-// in fp32; the state entering each chunk is stored (half, transposed [e][d]).
+// Phase 2: boundary-state scan. Every state element (d, e) of one (batch,
+// head) is its own first-order recurrence over the chunks,
+//   S_0 = given or 0,  S_{n+1}[d][e] = a_n[d] * S_n[d][e] + U_n[d][e],
+// and the step (a, U) composes associatively:
+//   (a1, U1) then (a2, U2) = (a2 a1, a2 U1 + U2).
+// So the chunk axis is cut into 16 segments, one per lane of a DPP row:
+// each lane folds its segment into one (a, U) pair, a 4-step row scan gives
+// every segment the composition of all earlier ones, and each lane then
+// replays its segment from the exact entering state, storing S_n (half,
+// [dk][dv]) for the output phase. A lane covers 8 consecutive value columns
+// of one key dim, so it needs a single decay per chunk; the four rows of a
+// wave take four neighbouring element groups, so each chunk's loads and
+// stores are 64-byte runs. The state after the last chunk (the composition
+// over all 16 segments, applied to S_0) is optionally written in fp32.
 // ===========================================================================
+constexpr int kScanSegs = 16;  // segments per chain: the lanes of a DPP row
+constexpr int kScanRegs = 8;   // chunks per segment kept in registers
+
+__device__ __forceinline__ void load_f8(const float* p, float (&a)[8]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  const float4 y = *reinterpret_cast<const float4*>(p + 4);
+  a[0] = x.x, a[1] = x.y, a[2] = x.z, a[3] = x.w;
+  a[4] = y.x, a[5] = y.y, a[6] = y.z, a[7] = y.w;
+}
+
+__device__ __forceinline__ void store_f8(float* p, const float (&a)[8]) {
+  *reinterpret_cast<float4*>(p) = float4{a[0], a[1], a[2], a[3]};
+  *reinterpret_cast<float4*>(p + 4) = float4{a[4], a[5], a[6], a[7]};
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_shr(float x, float fill) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict__ Uws,
                                                         const float* __restrict__ Aws,
-                                                        half_t* __restrict__ Sws, int N,
-                                                        int DK, int DKDV) {
-  constexpr int PF = 8;  // chunks per pipeline stage; two stages in flight
-  const long bh = blockIdx.y;
-  const int x = blockIdx.x * kThreads + threadIdx.x;
-  const int d = x % DK;
-  const half_t* U = Uws + bh * N * (long)DKDV + x;
-  const float* A = Aws + bh * N * (long)DK + d;
-  half_t* S = Sws + bh * N * (long)DKDV + x;
-  // loads use indices clamped to the last chunk, so they are always in
-  // bounds; values past the end are never consumed
-  auto fetch = [&](int n0, float (&u)[PF], float (&a)[PF]) {
+                                                        half_t* __restrict__ Sws,
+                                                        const float* __restrict__ s0,
+                                                        float* __restrict__ sfin, int H, int N,
+                                                        int DK, int DV, int L) {
+  const long bh = (long)blockIdx.z * H + blockIdx.y;
+  const int seg = threadIdx.x & (kScanSegs - 1);
+  const int x8 = 8 * (blockIdx.x * (kThreads / kScanSegs) + (threadIdx.x >> 4));
+  const int d = x8 / DV;
+  const long DKDV = (long)DK * DV;
+  const half_t* U = Uws + bh * N * DKDV + x8;
+  const float* A = Aws + bh * N * DK + d;
+  half_t* S = Sws + bh * N * DKDV + x8;
+  const int n0 = min(seg * L, N), n1 = min(n0 + L, N);
+
+  // -- fold this segment into (ag, ug); the chunks of one register block stay cached
+  float ag = 1.f, ug[8];
+  half8 uc[kScanRegs];
+  float ac[kScanRegs];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const long m = min(n0 + i, N - 1);
-      u[i] = (float)U[m * DKDV];
-      a[i] = A[m * DK];
-    }
-  };
-  float s = 0.f;
-  float u0[PF], a0[PF], u1[PF], a1[PF];
-  fetch(0, u0, a0);
-  for (int n = 0; n < N; n += 2 * PF) {
-    fetch(n + PF, u1, a1);
+  for (int c = 0; c < 8; ++c) ug[c] = 0.f;
+  for (int nb = n0; nb < n1; nb += kScanRegs) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      if (n + i < N) {
-        S[(long)(n + i) * DKDV] = (half_t)s;
-        s = a0[i] * s + u0[i];
+    for (int i = 0; i < kScanRegs; ++i) {
+      if (nb + i < n1) {
+        uc[i] = *reinterpret_cast<const half8*>(U + (long)(nb + i) * DKDV);
+        ac[i] = A[(long)(nb + i) * DK];
       }
     }
-    fetch(n + 2 * PF, u0, a0);
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      if (n + PF + i < N) {
-        S[(long)(n + PF + i) * DKDV] = (half_t)s;
-        s = a1[i] * s + u1[i];
+    for (int i = 0; i < kScanRegs; ++i) {
+      if (nb + i < n1) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ug[c] = ac[i] * ug[c] + (float)uc[i][c];
+        ag *= ac[i];
+      }
+    }
+  }
+  // -- inclusive composition over the segments of this row, then shift by one
+#define GLA_SCAN_STEP(CTRL)                                              \
+  {                                                                      \
+    const float ap = dpp_row_shr<CTRL>(ag, 1.f);                         \
+    _Pragma("unroll") for (int c = 0; c < 8; ++c) ug[c] =                \
+        ag * dpp_row_shr<CTRL>(ug[c], 0.f) + ug[c];                      \
+    ag *= ap;                                                            \
+  }
+  GLA_SCAN_STEP(0x111)
+  GLA_SCAN_STEP(0x112)
+  GLA_SCAN_STEP(0x114)
+  GLA_SCAN_STEP(0x118)
+#undef GLA_SCAN_STEP
+  float st0[8], s[8];
+  if (s0) {
+    load_f8(s0 + bh * DKDV + x8, st0);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st0[c] = 0.f;
+  }
+  const float ae = dpp_row_shr<0x111>(ag, 1.f);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s[c] = ae * st0[c] + dpp_row_shr<0x111>(ug[c], 0.f);
+  if (sfin && seg == kScanSegs - 1) {
+    float f[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) f[c] = ag * st0[c] + ug[c];
+    store_f8(sfin + bh * DKDV + x8, f);
+  }
+  // -- replay the segment from its entering state; a segment longer than one
+  // register block reads its chunks again (the registers hold the last block)
+  const bool cached = n1 - n0 <= kScanRegs;
+  for (int nb = n0; nb < n1; nb += kScanRegs) {
+    if (!cached) {
+#pragma unroll
+      for (int i = 0; i < kScanRegs; ++i) {
+        if (nb + i < n1) {
+          uc[i] = *reinterpret_cast<const half8*>(U + (long)(nb + i) * DKDV);
+          ac[i] = A[(long)(nb + i) * DK];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) {
+      if (nb + i < n1) {
+        store8(S + (long)(nb + i) * DKDV, s);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = ac[i] * s[c] + (float)uc[i][c];
       }
     }
   }
@@ -317,13 +397,16 @@ __global__ __launch_bounds__(kThreads, 4) void output_kernel(
     load_row<DK, NKS>(kp, row, lk, kf);
     load_row<DK, NKS>(gp, row, lk, sc);
   }
-  // -- the entering state S^T and the chunk's V^T, through LDS
+  // -- the entering state (stored [dk][dv], staged transposed as sS[e][d])
+  // and the chunk's V^T, through LDS
   {
     const long bhn = ((long)b * H + h) * N + n;
     const half_t* Sb = Sws + bhn * (long)(DV * DK);
-    for (int u = tid; u < DV * (DK / 8); u += kThreads) {
-      const int e = u / (DK / 8), d8 = (u % (DK / 8)) * 8;
-      *reinterpret_cast<half8*>(&sS[e][d8]) = load8h(Sb + e * DK + d8);
+    for (int u = tid; u < DK * (DV / 8); u += kThreads) {
+      const int d = u / (DV / 8), e8 = (u % (DV / 8)) * 8;
+      const half8 h8 = load8h(Sb + d * DV + e8);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sS[e8 + c][d] = h8[c];
     }
   }
   load_vt<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sVt);
@@ -573,15 +656,21 @@ hipError_t launch_summaries(const Problem& p, int b0, int nb, const DirPack& dir
   GLA_DISPATCH(summaries_t, p, b0, nb, dirs, k, v, gk, ws, s);
 }
 
-hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, hipStream_t s) {
+hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* s0,
+                       float* sfin, hipStream_t s) {
   const WsLayout w = workspace_layout(p);
   const long bhn = (long)b0 * p.H * p.N;
-  const int dkdv = p.dk * p.dv;
-  dim3 grid(dkdv / kThreads, nb * p.H);
+  const long dkdv = (long)p.dk * p.dv;
+  const long st = (long)b0 * p.H * dkdv;
+  const int L = (p.N + kScanSegs - 1) / kScanSegs;
+  // 16 element groups of 8 per workgroup; dk*dv is a multiple of 1024
+  dim3 grid((unsigned)(dkdv / (8 * (kThreads / kScanSegs))), p.H, nb);
   hipLaunchKernelGGL(scan_kernel, grid, dim3(kThreads), 0, s,
                      reinterpret_cast<const half_t*>(ws + w.off_U) + bhn * dkdv,
                      reinterpret_cast<const float*>(ws + w.off_a) + bhn * p.dk,
-                     reinterpret_cast<half_t*>(ws + w.off_S) + bhn * dkdv, p.N, p.dk, dkdv);
+                     reinterpret_cast<half_t*>(ws + w.off_S) + bhn * dkdv,
+                     s0 ? s0 + st : nullptr, sfin ? sfin + st : nullptr, p.H, p.N, p.dk, p.dv,
+                     L);
   return hipGetLastError();
 }
 

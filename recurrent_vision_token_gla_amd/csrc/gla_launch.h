@@ -27,7 +27,9 @@ WsLayout workspace_layout(const Problem& p);
 hipError_t launch_summaries(const Problem& p, int b0, int nb, const DirPack& dirs,
                             const void* k, const void* v, const void* gk, char* ws,
                             hipStream_t s);
-hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, hipStream_t s);
+// s0 / sfin (nullable) are the full-problem [B][H][dk][dv] fp32 state arrays.
+hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* s0,
+                       float* sfin, hipStream_t s);
 hipError_t launch_outputs(const Problem& p, int b0, int nb, const DirPack& dirs,
                           const void* q, const void* k, const void* v, const void* gk,
                           void* o, const char* ws, hipStream_t s);

@@ -20,7 +20,7 @@ OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 # every symbol declared in include/gla.h
 EXPORTS = ["gla_abi_version", "gla_fwd_workspace_bytes", "gla_workspace_layout", "gla_fwd",
-           "gla_chunk_summaries", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
+           "gla_fwd_state", "gla_chunk_summaries", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
            "gla_status_string", "gla_last_error_detail"]
 
 _lib = None
@@ -53,10 +53,13 @@ def load():
     lib.gla_workspace_layout.argtypes = [_i32] * 7 + [ctypes.POINTER(_sz)] * 4
     lib.gla_fwd.restype = _i32
     lib.gla_fwd.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
+    lib.gla_fwd_state.restype = _i32
+    lib.gla_fwd_state.argtypes = ([_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _vp, _vp, _sz,
+                                                            _vp])
     lib.gla_chunk_summaries.restype = _i32
     lib.gla_chunk_summaries.argtypes = [_vp] * 3 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
     lib.gla_state_scan.restype = _i32
-    lib.gla_state_scan.argtypes = [_i32] * 7 + [_vp, _sz, _vp]
+    lib.gla_state_scan.argtypes = [_i32] * 7 + [_vp, _vp, _vp, _sz, _vp]
     lib.gla_chunk_outputs.restype = _i32
     lib.gla_chunk_outputs.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
     lib.gla_scan_perm.restype = _i32
@@ -151,6 +154,41 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
     return out
 
 
+def _state_ptr(t: Optional[torch.Tensor], B, H, dk, dv, name) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if tuple(t.shape) != (B, H, dk, dv):
+        raise ValueError(f"{name} must be [B, H, dk, dv] = {(B, H, dk, dv)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def fwd_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
+              grid_h: int, grid_w: int, direction: Union[int, Sequence[int]] = L2R,
+              chunk: int = 64, s0: Optional[torch.Tensor] = None,
+              s_final: Optional[torch.Tensor] = None, return_state: bool = True,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None):
+    """Forward from the carried state s0 ([B, H, dk, dv] float32, None for
+    zero); returns (o, S_T) with S_T written into s_final (allocated if None)
+    when return_state, else o."""
+    B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if return_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
+    st = load().gla_fwd_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                              out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
+                              chunk, _dtype_code(q), _state_ptr(s0, B, H, dk, dv, "s0"),
+                              _state_ptr(s_final, B, H, dk, dv, "s_final"),
+                              workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _check(st, "gla_fwd_state")
+    return (out, s_final) if return_state else out
+
+
 def chunk_summaries(k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspace=None,
                     stream=None) -> torch.Tensor:
     """Phase 1 only; returns the workspace holding U and a."""
@@ -164,9 +202,12 @@ def chunk_summaries(k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspace
     return workspace
 
 
-def state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace, stream=None) -> torch.Tensor:
-    st = load().gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace.data_ptr(),
-                               workspace.numel(), _stream_ptr(stream))
+def state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace, s0=None, s_final=None,
+               stream=None) -> torch.Tensor:
+    st = load().gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk,
+                               _state_ptr(s0, B, H, dk, dv, "s0"),
+                               _state_ptr(s_final, B, H, dk, dv, "s_final"),
+                               workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
     _check(st, "gla_state_scan")
     return workspace
 
@@ -185,13 +226,13 @@ def chunk_outputs(q, k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspac
 
 
 def workspace_views(workspace: torch.Tensor, B, H, grid_h, grid_w, dk, dv, chunk=64):
-    """Views of U [B,H,N,dv,dk] f16, a [B,H,N,dk] f32, S [B,H,N,dv,dk] f16."""
+    """Views of U [B,H,N,dk,dv] f16, a [B,H,N,dk] f32, S [B,H,N,dk,dv] f16."""
     off_U, off_a, off_S, _ = workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk)
     N = -(-(grid_h * grid_w) // chunk)
     n_us = B * H * N * dk * dv
-    U = workspace[off_U:off_U + 2 * n_us].view(torch.float16).view(B, H, N, dv, dk)
+    U = workspace[off_U:off_U + 2 * n_us].view(torch.float16).view(B, H, N, dk, dv)
     a = workspace[off_a:off_a + 4 * B * H * N * dk].view(torch.float32).view(B, H, N, dk)
-    S = workspace[off_S:off_S + 2 * n_us].view(torch.float16).view(B, H, N, dv, dk)
+    S = workspace[off_S:off_S + 2 * n_us].view(torch.float16).view(B, H, N, dk, dv)
     return U, a, S
 
 

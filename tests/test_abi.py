@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gla_abi_version() == 1
+    assert lib.gla_abi_version() == 2
     for st in (0, -1, -2, -3, -4, 7):
         s = lib.gla_status_string(st)
         assert s and isinstance(s, bytes)
@@ -93,6 +93,26 @@ def test_argument_errors_before_any_launch(lib):
     assert lib.gla_last_error_detail() == b""
 
 
+def _fwd_state(lib, s0=None, sf=None, q=FAKE, o=FAKE + 0x4000, ws=FAKE + 0x5000, ws_bytes=10 ** 6):
+    arr = (ctypes.c_int32 * 1)(0)
+    return lib.gla_fwd_state(q, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, o, 1, 1, 4, 4, 32, 32,
+                             arr, 16, 0, s0, sf, ws, ws_bytes, None)
+
+
+def test_carried_state_argument_errors(lib):
+    assert _fwd_state(lib, s0=FAKE + 0x6002) == gla.E_ARG      # misaligned s0
+    assert _fwd_state(lib, sf=FAKE + 0x6004) == gla.E_ARG      # misaligned s_final
+    assert _fwd_state(lib, sf=FAKE) == gla.E_ARG               # s_final aliases q
+    assert _fwd_state(lib, sf=FAKE + 0x4000) == gla.E_ARG      # s_final aliases o
+    assert _fwd_state(lib, sf=FAKE + 0x5000) == gla.E_ARG      # s_final aliases the workspace
+    assert _fwd_state(lib, q=None, s0=FAKE + 0x6000) == gla.E_ARG
+    assert _fwd_state(lib, s0=FAKE + 0x6000, ws_bytes=1) == gla.E_WORKSPACE
+    # empty problem: nothing examined
+    arr = (ctypes.c_int32 * 1)(0)
+    assert lib.gla_fwd_state(None, None, None, None, None, 0, 1, 4, 4, 32, 32, arr, 16, 0, None,
+                             None, None, 0, None) == gla.OK
+
+
 def test_empty_problems_are_noops(lib):
     # nothing to compute: returns OK and does not look at the pointers
     assert _fwd(lib, q=None, k=None, v=None, g=None, o=None, ws=None, B=0, dirs=None) == gla.OK
@@ -105,8 +125,13 @@ def test_phase_entry_points_validate(lib):
     arr = (ctypes.c_int32 * 1)(0)
     assert lib.gla_chunk_summaries(None, FAKE, FAKE, 1, 1, 4, 4, 32, 32, arr, 16, 0, FAKE, 10 ** 6,
                                    None) == gla.E_ARG
-    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 16, FAKE, 1, None) == gla.E_WORKSPACE
-    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 24, FAKE, 10 ** 6, None) == gla.E_UNSUPPORTED
+    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 16, None, None, FAKE, 1, None) == gla.E_WORKSPACE
+    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 24, None, None, FAKE, 10 ** 6,
+                              None) == gla.E_UNSUPPORTED
+    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 16, FAKE + 4, None, FAKE, 10 ** 6,
+                              None) == gla.E_ARG          # misaligned s0
+    assert lib.gla_state_scan(1, 1, 4, 4, 32, 32, 16, None, FAKE + 8, FAKE, 10 ** 6,
+                              None) == gla.E_ARG          # misaligned s_final
     assert lib.gla_chunk_outputs(FAKE, FAKE + 0x100, FAKE + 0x200, FAKE + 0x300, FAKE + 0x100, 1, 1,
                                  4, 4, 32, 32, arr, 16, 0, FAKE, 10 ** 6, None) == gla.E_ARG
     assert lib.gla_scan_perm(FAKE, 4, 4, 7, None) == gla.E_ARG
