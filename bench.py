@@ -49,16 +49,20 @@ def per_unit_bytes(w):
 
 
 def phase_bytes(w):
-    """Bytes each phase must move in the three-kernel schedule, per launch.
+    """Algorithmic bytes each kernel must move per launch.
 
-    summaries: read k, gk, v; write U (f16 dk*dv) and a (f32 dk) per chunk-head
-    scan:      read U and a; write S (f16 dk*dv) per chunk-head
-    outputs:   read q, k, gk, v and S; write o
+    single_pass: read q, k, gk, v; write o (the whole forward's own I/O; the
+                 chunk summaries it publishes to its successors are not
+                 counted)
+    summaries:   read k, gk, v; write U (f16 dk*dv) and a (f32 dk) per chunk-head
+    scan:        read U and a; write S (f16 dk*dv) per chunk-head
+    outputs:     read q, k, gk, v and S; write o
     """
     e = 2 if w.dtype == "f16" else 4
     th = w.B * w.T * w.H
     ch = w.B * w.H * math.ceil(w.T / w.chunk)
     return {
+        "single_pass": th * per_unit_bytes(w),
         "summaries": th * (2 * w.dk + w.dv) * e + ch * (2 * w.dk * w.dv + 4 * w.dk),
         "scan": ch * (2 * w.dk * w.dv + 4 * w.dk + 2 * w.dk * w.dv),
         "outputs": th * (3 * w.dk + 2 * w.dv) * e + ch * 2 * w.dk * w.dv,
@@ -138,13 +142,18 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
         b.synchronize()
         lat.append(a.elapsed_time(b) * 1e3)
 
-    # per-phase kernel durations: each phase alone, `timing_reps` launches
-    # captured back to back in one graph (no host gaps), timed with events on
-    # the stream the kernels are launched on
+    # per-kernel durations: each kernel alone, `timing_reps` launches captured
+    # back to back in one graph (no host gaps), timed with events on the
+    # stream the kernels are launched on. The step's own schedule is the one
+    # gla_fwd picks; the other schedule's kernels are timed for reference.
     c0 = calls[0]
+    sched = gla.auto_schedule(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk)
 
     def phases(s):
         return {
+            "single_pass": lambda: gla.fwd(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
+                                           c0["dirs"], w.chunk, out=c0["out"], workspace=ws,
+                                           stream=s, schedule=gla.SCHED_SINGLE_PASS),
             "summaries": lambda: gla.chunk_summaries(c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
                                                      c0["dirs"], w.chunk, workspace=ws, stream=s),
             "scan": lambda: gla.state_scan(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, ws,
@@ -155,10 +164,15 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
         }
 
     phase_us = {}
-    for name in ("summaries", "scan", "outputs"):
+    for name in ("single_pass", "summaries", "scan", "outputs"):
         s = torch.cuda.Stream()
         s.wait_stream(stream)
         fn = phases(s)[name]
+        if name == "single_pass":
+            try:
+                fn()  # rejected on the host (nothing launched) if it does not fit
+            except gla.GLAError:
+                continue
         pg = torch.cuda.CUDAGraph()
         with torch.cuda.stream(s):
             fn()
@@ -180,8 +194,10 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
     # the full step ran last on the workspace: re-run it so outputs are current
     run()
     torch.cuda.synchronize()
+    used = ["single_pass"] if sched == gla.SCHED_SINGLE_PASS else ["summaries", "scan", "outputs"]
     return dict(calls=calls, ms_per_step=ms_per_step, wall_s=wall, lat_us=lat,
-                phase_us=phase_us, ws=ws)
+                phase_us=phase_us, ws=ws, used=used,
+                schedule="single_pass" if sched == gla.SCHED_SINGLE_PASS else "three_phase")
 
 
 def parity_check(w, res, oracle, np, max_bh=4):
@@ -226,7 +242,8 @@ def summarize(w, res):
     path_bytes_call = th_call * per_unit_bytes(w)
     call_us = res["ms_per_step"] * 1e3 / w.calls
     pb = phase_bytes(w)
-    dom = max(res["phase_us"], key=res["phase_us"].get)
+    used = {k: res["phase_us"][k] for k in res["used"]}
+    dom = max(used, key=used.get)
     ach = pb[dom] / (res["phase_us"][dom] * 1e-6) / 1e9
     return {
         "value": value,
@@ -243,6 +260,7 @@ def summarize(w, res):
                      "kernel": dom, "algorithmic_bytes_per_launch": pb[dom],
                      "avg_launch_us": res["phase_us"][dom]},
         "phase_us": res["phase_us"],
+        "schedule": res["schedule"],
     }
 
 
@@ -293,7 +311,7 @@ def main():
     res = run_workload(w, args.steps, args.warmup, not args.no_graph, torch, gla, W)
     s = summarize(w, res)
     print(f"# {w.name}: {s['value']:.4g} tokens/s, {s['call_us']:.2f} us/call, "
-          f"path {100 * s['path_roofline']['frac']:.1f}% of HBM roofline, phases "
+          f"path {100 * s['path_roofline']['frac']:.1f}% of HBM roofline, {s['schedule']}; kernels "
           + ", ".join(f"{k} {v:.2f} us" for k, v in s["phase_us"].items()),
           file=sys.stderr, flush=True)
 
@@ -316,14 +334,14 @@ def main():
                           not args.no_graph, torch, gla, W)
         si = summarize(wi, ri)
         print(f"# {wi.name}: {si['value']:.4g} tokens/s, {si['call_us']:.2f} us/call, path "
-              f"{100 * si['path_roofline']['frac']:.1f}% of HBM roofline, phases "
+              f"{100 * si['path_roofline']['frac']:.1f}% of HBM roofline, {si['schedule']}; kernels "
               + ", ".join(f"{k} {v:.2f} us" for k, v in si["phase_us"].items()),
               file=sys.stderr, flush=True)
         also.append({"workload": wi.name, "tokens_per_call": wi.B * wi.T,
                      "value": si["value"], "unit": "tokens/s", "us_per_call": si["call_us"],
                      "path_roofline_frac": si["path_roofline"]["frac"],
-                     "dominant": si["dominant"], "dominant_frac": si["roofline"]["frac"],
-                     "phase_us": si["phase_us"]})
+                     "schedule": si["schedule"], "dominant": si["dominant"],
+                     "dominant_frac": si["roofline"]["frac"], "kernel_us": si["phase_us"]})
         del ri
         torch.cuda.empty_cache()
 
@@ -347,7 +365,8 @@ def main():
         "roofline": s["roofline"],
         "path_roofline": s["path_roofline"],
         "median_step_latency_us": s["median_step_latency_us"],
-        "phase_us": s["phase_us"],
+        "schedule": s["schedule"],
+        "kernel_us": s["phase_us"],
         "parity_max_rel_err": parity,
         "cpu_baseline": cpu,
         "also": also,

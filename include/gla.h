@@ -15,9 +15,10 @@
  * log of the per-key-dimension decay (gk <= 0 is the contract; gk > 0 makes
  * the state grow and may overflow). No query scaling is applied.
  *
- * How it is computed: the "same state update, different execution schedule"
- * of the project page's kernel section. Tokens are cut into chunks of
- * `chunk` tokens. Three kernels run back to back on the caller's stream:
+ * How it is computed: the chunkwise form, which the project page's kernel
+ * section presents as the recurrence itself on another execution order.
+ * Tokens are cut into chunks of `chunk` tokens. The three-phase schedule
+ * runs three kernels back to back on the caller's stream:
  *   1. chunk summaries   -- for every (chunk, head) in parallel: the chunk's
  *                           total decay a_n and its state contribution U_n;
  *   2. boundary scan     -- S_{n+1} = diag(a_n) S_n + U_n along the chunks;
@@ -39,11 +40,29 @@
  * raster order; top->bottom walks the columns left to right, each column top
  * to bottom; right->left and bottom->top are the full reversals of those.
  *
+ * Schedules: besides the three kernels above, the forward can run as ONE
+ * kernel (single pass): every (chunk, head) workgroup computes its summary,
+ * publishes it, computes its intra-chunk part, then takes its entering state
+ * from the summaries its predecessors publish (grouped in about sqrt(N)
+ * segments, whose last chunks publish segment aggregates), and adds the
+ * readout. Workgroups run in chain-major order and only wait on earlier
+ * ones, with bounded waits. gla_fwd picks the single pass for chains of at
+ * most 36 chunks (if the launch fits its control words) and the three
+ * phases for longer chains.
+ *
+ * Workspace: caller-owned device memory of gla_fwd_workspace_bytes bytes,
+ * 256-byte aligned. Its first 64 KiB are control words of the single pass;
+ * they must be ZERO before the workspace is first used (gla_workspace_init,
+ * or any zero fill), and every call leaves them zero again, also when the
+ * workspace is later used for another problem size. Word 0 is a sticky
+ * error word: bit 0 set means a single-pass wait ran out of its poll budget
+ * (results of that call are invalid); gla_workspace_init clears it.
+ *
  * Execution: asynchronous on `stream` (a hipStream_t passed as void*; NULL
  * is the default stream). No call allocates, synchronises or reads device
  * memory on the host, so every call can be captured in a HIP graph. Calls
- * are stateless and may run concurrently on different workspaces. The
- * library keeps no pointer after a call returns.
+ * are stateless and may run concurrently on different workspaces (never on
+ * one workspace). The library keeps no pointer after a call returns.
  *
  * Errors: arguments are checked on the host before any HIP call; a failing
  * check returns a negative status and touches nothing. A failed launch
@@ -64,6 +83,7 @@ extern "C" {
 
 enum { GLA_L2R = 0, GLA_R2L = 1, GLA_T2B = 2, GLA_B2T = 3 };
 enum { GLA_F16 = 0, GLA_F32 = 1 };
+enum { GLA_SCHED_AUTO = 0, GLA_SCHED_SINGLE_PASS = 1, GLA_SCHED_THREE_PHASE = 2 };
 enum {
   GLA_OK = 0,
   GLA_E_ARG = -1,          /* null/misaligned pointer, negative size, bad code */
@@ -75,6 +95,12 @@ enum {
 /* Library ABI version (incremented on any signature or layout change). */
 int gla_abi_version(void);
 
+/* Zero the workspace's control words (its first 64 KiB) with a kernel on
+ * `stream` (graph-capturable). Needed once per workspace before its first
+ * use; also clears the sticky error word. workspace_bytes is the size of the
+ * buffer (at least 64 KiB). */
+int gla_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace gla_fwd needs for this problem (0 for an empty one, or
  * if the shape is unsupported or negative). */
 size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk,
@@ -82,9 +108,10 @@ size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk,
 
 /* Byte offsets, within the workspace, of the three intermediate arrays, so
  * that callers (tests) can inspect them after the phase calls below:
- *   U : half  [B][H][N][dk][dv]   chunk summaries
+ *   U : half  [B][H][N][dk][dv]   chunk summaries (both schedules)
  *   a : float [B][H][N][dk]       per-chunk total decay exp(sum of gk)
- *   S : half  [B][H][N][dk][dv]   state entering each chunk
+ *   S : half  [B][H][N][dk][dv]   state entering each chunk (three phases;
+ *                                 the single pass keeps segment aggregates)
  * with N = ceil(T / chunk). Returns GLA_OK or GLA_E_ARG/GLA_E_UNSUPPORTED. */
 int gla_workspace_layout(int B, int H, int grid_h, int grid_w, int dk, int dv,
                          int chunk, size_t* off_U, size_t* off_a,
@@ -116,6 +143,23 @@ int gla_fwd_state(const void* q, const void* k, const void* v, const void* gk,
                   const int32_t* dir, int chunk, int dtype, const float* s0,
                   float* s_final, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* gla_fwd_state with an explicit schedule: GLA_SCHED_AUTO (what gla_fwd and
+ * gla_fwd_state do), GLA_SCHED_SINGLE_PASS (returns GLA_E_UNSUPPORTED if the
+ * problem does not fit its control words: more than 4096 chunks per chain,
+ * or more chunk-heads per launch than the 64 KiB hold) or
+ * GLA_SCHED_THREE_PHASE. Results agree up to rounding. */
+int gla_fwd_schedule(const void* q, const void* k, const void* v,
+                     const void* gk, void* o, int B, int H, int grid_h,
+                     int grid_w, int dk, int dv, const int32_t* dir, int chunk,
+                     int dtype, const float* s0, float* s_final, int schedule,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The schedule gla_fwd and gla_fwd_state take for this shape
+ * (GLA_SCHED_SINGLE_PASS or GLA_SCHED_THREE_PHASE; the dtype does not
+ * matter), or GLA_E_ARG / GLA_E_UNSUPPORTED for a bad shape. */
+int gla_auto_schedule(int B, int H, int grid_h, int grid_w, int dk, int dv,
+                      int chunk);
 
 /* Phase 1 alone: chunk summaries into the workspace's U and a (for every
  * (chunk, head) in parallel; ai.info summary of GTR, "Methodology in Plain

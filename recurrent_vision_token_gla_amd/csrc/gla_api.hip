@@ -69,11 +69,67 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
     if (rc_ != GLA_OK) return rc_; \
   } while (0)
 
+// Auto dispatch: the single pass saves two kernel boundaries and one read of
+// k, v, gk, but every chunk reads O(sqrt(N)) published tiles; measured on
+// MI355X it is ahead up to 36 chunks per chain (any batch) and behind from
+// about 50 on, so chains longer than 36 chunks take the three phases.
+constexpr int kOnepassMaxChain = 36;
+
+bool single_pass_fits(const gla::Problem& p) {
+  const int nb_max = p.B < gla::kMaxBatchPerLaunch ? p.B : gla::kMaxBatchPerLaunch;
+  return gla::onepass_fits(p, nb_max);
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
+             int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
+             const float* s0, float* s_final, void* workspace, size_t workspace_bytes,
+             void* stream, int mode /* 0 auto, 1 single pass, 2 three phases */) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
+  if (empty) return GLA_OK;
+  // validate everything before the first launch so that a bad call enqueues nothing
+  GLA_TRY(check_tensor(q));
+  GLA_TRY(check_tensor(k));
+  GLA_TRY(check_tensor(v));
+  GLA_TRY(check_tensor(gk));
+  GLA_TRY(check_tensor(o));
+  if (o == q || o == k || o == v || o == gk) return GLA_E_ARG;
+  if (s0) GLA_TRY(check_tensor(s0));
+  if (s_final) {
+    GLA_TRY(check_tensor(s_final));
+    const void* sf = s_final;
+    if (sf == q || sf == k || sf == v || sf == gk || sf == o || sf == workspace) return GLA_E_ARG;
+  }
+  GLA_TRY(check_dirs(dir, B));
+  GLA_TRY(check_ws(p, workspace, workspace_bytes));
+  bool onepass = single_pass_fits(p);
+  if (mode == 1 && !onepass) return GLA_E_UNSUPPORTED;
+  if (mode == 0) onepass = onepass && p.N <= kOnepassMaxChain;
+  if (mode == 2) onepass = false;
+  if (onepass) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
+      const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
+      const hipError_t e = gla::launch_onepass(p, b0, nb, pack_dirs(dir, b0, nb), q, k, v, gk, o,
+                                               static_cast<char*>(workspace), s0, s_final, s);
+      if (e != hipSuccess) return fail_hip(e, "single-pass launch");
+    }
+    return GLA_OK;
+  }
+  GLA_TRY(gla_chunk_summaries(k, v, gk, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
+                              workspace, workspace_bytes, stream));
+  GLA_TRY(gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, s0, s_final, workspace,
+                         workspace_bytes, stream));
+  return gla_chunk_outputs(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
+                           workspace, workspace_bytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
-int gla_abi_version(void) { return 2; }
+int gla_abi_version(void) { return 3; }
 
 size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv,
                                int chunk) {
@@ -168,42 +224,48 @@ int gla_chunk_outputs(const void* q, const void* k, const void* v, const void* g
   return GLA_OK;
 }
 
+int gla_fwd(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
+            int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, nullptr,
+                  nullptr, workspace, workspace_bytes, stream, 0);
+}
+
 int gla_fwd_state(const void* q, const void* k, const void* v, const void* gk, void* o, int B,
                   int H, int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk,
                   int dtype, const float* s0, float* s_final, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  gla::Problem p;
-  bool empty;
-  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
-  if (empty) return GLA_OK;
-  // validate everything before the first launch so that a bad call enqueues nothing
-  GLA_TRY(check_tensor(q));
-  GLA_TRY(check_tensor(k));
-  GLA_TRY(check_tensor(v));
-  GLA_TRY(check_tensor(gk));
-  GLA_TRY(check_tensor(o));
-  if (o == q || o == k || o == v || o == gk) return GLA_E_ARG;
-  if (s0) GLA_TRY(check_tensor(s0));
-  if (s_final) {
-    GLA_TRY(check_tensor(s_final));
-    const void* sf = s_final;
-    if (sf == q || sf == k || sf == v || sf == gk || sf == o || sf == workspace) return GLA_E_ARG;
-  }
-  GLA_TRY(check_dirs(dir, B));
-  GLA_TRY(check_ws(p, workspace, workspace_bytes));
-  GLA_TRY(gla_chunk_summaries(k, v, gk, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
-                              workspace, workspace_bytes, stream));
-  GLA_TRY(gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, s0, s_final, workspace,
-                         workspace_bytes, stream));
-  return gla_chunk_outputs(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
-                           workspace, workspace_bytes, stream);
+  return fwd_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, s0, s_final,
+                  workspace, workspace_bytes, stream, 0);
 }
 
-int gla_fwd(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
-            int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
-            void* workspace, size_t workspace_bytes, void* stream) {
-  return gla_fwd_state(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, nullptr,
-                       nullptr, workspace, workspace_bytes, stream);
+int gla_fwd_schedule(const void* q, const void* k, const void* v, const void* gk, void* o, int B,
+                     int H, int grid_h, int grid_w, int dk, int dv, const int32_t* dir,
+                     int chunk, int dtype, const float* s0, float* s_final, int schedule,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (schedule != GLA_SCHED_AUTO && schedule != GLA_SCHED_SINGLE_PASS &&
+      schedule != GLA_SCHED_THREE_PHASE)
+    return GLA_E_ARG;
+  return fwd_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, s0, s_final,
+                  workspace, workspace_bytes, stream, schedule);
+}
+
+int gla_auto_schedule(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, GLA_F16, &p, &empty));
+  if (empty) return GLA_SCHED_THREE_PHASE;
+  return single_pass_fits(p) && p.N <= kOnepassMaxChain ? GLA_SCHED_SINGLE_PASS
+                                                        : GLA_SCHED_THREE_PHASE;
+}
+
+int gla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return GLA_E_ARG;
+  if (workspace_bytes < (size_t)gla::kCtrlWords * sizeof(unsigned)) return GLA_E_WORKSPACE;
+  const hipError_t e =
+      gla::launch_ctrl_clear(static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "workspace init launch");
+  return GLA_OK;
 }
 
 int gla_scan_perm(int32_t* perm_dev, int grid_h, int grid_w, int dir, void* stream) {

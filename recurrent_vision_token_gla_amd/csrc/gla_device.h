@@ -17,6 +17,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;          // 4 wave64 per workgroup
 constexpr int kMaxBatchPerLaunch = 1024;
 
+// Control words of the single-pass schedule, at the start of every workspace
+// (64 KiB): a header (word 0: sticky error bits) and, per (batch, head) chain
+// of a launch, one word per chunk, one per segment and one counter.
+constexpr int kCtrlWords = 16384;
+constexpr int kCtrlHeader = 64;
+
 // Direction codes of up to kMaxBatchPerLaunch batch elements, 2 bits each,
 // passed by value in the kernel arguments (no device copy, graph-safe).
 struct DirPack {

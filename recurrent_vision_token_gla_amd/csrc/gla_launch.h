@@ -15,12 +15,23 @@ struct Problem {
   int dtype;  // GLA_F16 or GLA_F32
 };
 
-// Byte offsets of the intermediate arrays inside the workspace.
+// Byte offsets of the arrays inside the workspace: the control words (fixed
+// size, offset 0), U, a, S (S also holds the single-pass segment aggregates)
+// and the single-pass segment decays.
 struct WsLayout {
-  size_t off_U, off_a, off_S, total;
+  size_t off_U, off_a, off_S, off_g, total;
 };
 
 WsLayout workspace_layout(const Problem& p);
+
+// Segments of the single-pass schedule: G chunks each (G = ceil(sqrt(N))).
+struct Segments {
+  int G, nseg;
+};
+Segments onepass_segments(int N);
+// Whether a launch of nb batch elements fits the single-pass schedule's
+// control words and wait width.
+bool onepass_fits(const Problem& p, int nb);
 
 // Each launcher enqueues one phase for batch elements [b0, b0 + nb) of the
 // problem (nb <= kMaxBatchPerLaunch); pointers are the full-problem bases.
@@ -33,6 +44,12 @@ hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* 
 hipError_t launch_outputs(const Problem& p, int b0, int nb, const DirPack& dirs,
                           const void* q, const void* k, const void* v, const void* gk,
                           void* o, const char* ws, hipStream_t s);
+// The whole forward in one kernel (requires onepass_fits(p, nb)).
+hipError_t launch_onepass(const Problem& p, int b0, int nb, const DirPack& dirs, const void* q,
+                          const void* k, const void* v, const void* gk, void* o, char* ws,
+                          const float* s0, float* sfin, hipStream_t s);
+// Zero the control words of a workspace (a fill kernel, graph-capturable).
+hipError_t launch_ctrl_clear(char* ws, hipStream_t s);
 hipError_t launch_scan_perm(int32_t* perm, int gh, int gw, int dir, hipStream_t s);
 
 }  // namespace gla

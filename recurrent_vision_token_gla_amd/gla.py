@@ -16,11 +16,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgla_mi35
 
 L2R, R2L, T2B, B2T = 0, 1, 2, 3
 F16, F32 = 0, 1
+SCHED_AUTO, SCHED_SINGLE_PASS, SCHED_THREE_PHASE = 0, 1, 2
+CTRL_BYTES = 65536  # control words at the start of every workspace
 OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 # every symbol declared in include/gla.h
 EXPORTS = ["gla_abi_version", "gla_fwd_workspace_bytes", "gla_workspace_layout", "gla_fwd",
-           "gla_fwd_state", "gla_chunk_summaries", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
+           "gla_fwd_state", "gla_fwd_schedule", "gla_auto_schedule", "gla_workspace_init",
+           "gla_chunk_summaries", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
            "gla_status_string", "gla_last_error_detail"]
 
 _lib = None
@@ -56,6 +59,13 @@ def load():
     lib.gla_fwd_state.restype = _i32
     lib.gla_fwd_state.argtypes = ([_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _vp, _vp, _sz,
                                                             _vp])
+    lib.gla_fwd_schedule.restype = _i32
+    lib.gla_fwd_schedule.argtypes = ([_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _vp, _i32,
+                                                               _vp, _sz, _vp])
+    lib.gla_auto_schedule.restype = _i32
+    lib.gla_auto_schedule.argtypes = [_i32] * 7
+    lib.gla_workspace_init.restype = _i32
+    lib.gla_workspace_init.argtypes = [_vp, _sz, _vp]
     lib.gla_chunk_summaries.restype = _i32
     lib.gla_chunk_summaries.argtypes = [_vp] * 3 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
     lib.gla_state_scan.restype = _i32
@@ -113,8 +123,30 @@ def workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk=64):
 
 
 def alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk=64, device=None) -> torch.Tensor:
+    """A workspace for this problem, zero-filled (its control words must start
+    at zero; every call leaves them zero)."""
     n = workspace_bytes(B, H, grid_h, grid_w, dk, dv, chunk)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+    return torch.zeros(max(n, CTRL_BYTES), dtype=torch.uint8, device=device or "cuda")
+
+
+def auto_schedule(B, H, grid_h, grid_w, dk, dv, chunk=64) -> int:
+    """The schedule gla_fwd takes for this shape (SCHED_SINGLE_PASS or
+    SCHED_THREE_PHASE)."""
+    st = load().gla_auto_schedule(B, H, grid_h, grid_w, dk, dv, chunk)
+    if st < 0:
+        raise GLAError(st, "gla_auto_schedule")
+    return st
+
+
+def workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    """Zero the control words (and the sticky error word) with a kernel."""
+    _check(load().gla_workspace_init(workspace.data_ptr(), workspace.numel(),
+                                     _stream_ptr(stream)), "gla_workspace_init")
+
+
+def workspace_error(workspace: torch.Tensor) -> int:
+    """The sticky error word (bit 0: a single-pass wait ran out). Syncs."""
+    return int(workspace[:4].view(torch.int32).item())
 
 
 def _shapes(q, k, v, gk, grid_h, grid_w):
@@ -140,18 +172,22 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
         grid_h: int, grid_w: int, direction: Union[int, Sequence[int]] = L2R,
         chunk: int = 64, out: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None,
-        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        stream: Optional[torch.cuda.Stream] = None, schedule: int = SCHED_AUTO) -> torch.Tensor:
     """o = key-only GLA forward along `direction` (int, or one per batch element)."""
     B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
-    st = load().gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), out.data_ptr(),
-                        B, H, grid_h, grid_w, dk, dv, _dirs(direction, B), chunk, _dtype_code(q),
-                        workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
-    _check(st, "gla_fwd")
-    return out
+    if schedule == SCHED_AUTO:
+        st = load().gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                            out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
+                            chunk, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                            _stream_ptr(stream))
+        _check(st, "gla_fwd")
+        return out
+    return fwd_state(q, k, v, gk, grid_h, grid_w, direction, chunk, return_state=False, out=out,
+                     workspace=workspace, stream=stream, schedule=schedule)
 
 
 def _state_ptr(t: Optional[torch.Tensor], B, H, dk, dv, name) -> Optional[int]:
@@ -169,10 +205,10 @@ def fwd_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tenso
               chunk: int = 64, s0: Optional[torch.Tensor] = None,
               s_final: Optional[torch.Tensor] = None, return_state: bool = True,
               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-              stream: Optional[torch.cuda.Stream] = None):
+              stream: Optional[torch.cuda.Stream] = None, schedule: int = SCHED_AUTO):
     """Forward from the carried state s0 ([B, H, dk, dv] float32, None for
     zero); returns (o, S_T) with S_T written into s_final (allocated if None)
-    when return_state, else o."""
+    when return_state, else o. schedule picks the kernel schedule."""
     B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
@@ -180,12 +216,13 @@ def fwd_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tenso
         s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
-    st = load().gla_fwd_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
-                              out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
-                              chunk, _dtype_code(q), _state_ptr(s0, B, H, dk, dv, "s0"),
-                              _state_ptr(s_final, B, H, dk, dv, "s_final"),
-                              workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
-    _check(st, "gla_fwd_state")
+    st = load().gla_fwd_schedule(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                                 out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
+                                 _dirs(direction, B), chunk, _dtype_code(q),
+                                 _state_ptr(s0, B, H, dk, dv, "s0"),
+                                 _state_ptr(s_final, B, H, dk, dv, "s_final"), schedule,
+                                 workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _check(st, "gla_fwd_schedule")
     return (out, s_final) if return_state else out
 
 

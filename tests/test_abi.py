@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gla_abi_version() == 2
+    assert lib.gla_abi_version() == 3
     for st in (0, -1, -2, -3, -4, 7):
         s = lib.gla_status_string(st)
         assert s and isinstance(s, bytes)
@@ -47,17 +47,18 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # U (f16) + a (f32) + S (f16), each padded to 256 bytes
+    # control words (64 KiB) + U (f16) + a (f32) + S (f16) + segment decays (f32),
+    # each padded to 256 bytes
     B, H, gh, gw, dk, dv, C = 1, 6, 40, 40, 64, 64, 64
     N = 25
     units = B * H * N
-    expect = units * dk * dv * 2 + units * dk * 4 + units * dk * dv * 2
+    expect = 65536 + units * dk * dv * 2 + units * dk * 4 + units * dk * dv * 2 + units * dk * 4
     assert gla.workspace_bytes(B, H, gh, gw, dk, dv, C) == expect
     assert gla.workspace_bytes(0, H, gh, gw, dk, dv, C) == 0
     assert gla.workspace_bytes(1, 1, 5, 7, 32, 32, 16) > 0
     assert gla.workspace_bytes(1, 1, 8, 8, 48, 32, 16) == 0  # unsupported dk
     off_U, off_a, off_S, total = gla.workspace_layout(B, H, gh, gw, dk, dv, C)
-    assert off_U == 0 and off_a % 256 == 0 and off_S % 256 == 0 and total == expect
+    assert off_U == 65536 and off_a % 256 == 0 and off_S % 256 == 0 and total == expect
 
 
 FAKE = 0x10000  # 256-aligned, never dereferenced: every call below fails validation first
@@ -137,3 +138,34 @@ def test_phase_entry_points_validate(lib):
     assert lib.gla_scan_perm(FAKE, 4, 4, 7, None) == gla.E_ARG
     assert lib.gla_scan_perm(None, 4, 4, 0, None) == gla.E_ARG
     assert lib.gla_scan_perm(FAKE + 1, 4, 4, 0, None) == gla.E_ARG
+
+
+def test_schedule_and_workspace_init_validate(lib):
+    arr = (ctypes.c_int32 * 1)(0)
+    big = 10 ** 12  # never allocated: every call below fails before any launch
+
+    def sched(schedule, gh=4, gw=4, chunk=16, ws_bytes=big):
+        return lib.gla_fwd_schedule(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
+                                    FAKE + 0x4000, 1, 1, gh, gw, 32, 32, arr, chunk, 0, None, None,
+                                    schedule, FAKE + 0x5000, ws_bytes, None)
+    assert sched(3) == gla.E_ARG
+    assert sched(-1) == gla.E_ARG
+    # 4097 chunks in one chain: more than the single pass waits on
+    assert sched(gla.SCHED_SINGLE_PASS, gh=4097, gw=16, chunk=16) == gla.E_UNSUPPORTED
+    assert sched(gla.SCHED_SINGLE_PASS, ws_bytes=100) == gla.E_WORKSPACE
+    assert lib.gla_workspace_init(None, 1 << 20, None) == gla.E_ARG
+    assert lib.gla_workspace_init(FAKE + 0x10, 1 << 20, None) == gla.E_ARG
+    assert lib.gla_workspace_init(FAKE, 65535, None) == gla.E_WORKSPACE
+
+
+def test_auto_schedule(lib):
+    # 25 chunks per chain: single pass; 100: three phases; 4097 chunks: three phases
+    assert gla.auto_schedule(1, 6, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    assert gla.auto_schedule(8, 12, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    assert gla.auto_schedule(1, 6, 80, 80, 64, 64, 64) == gla.SCHED_THREE_PHASE
+    assert gla.auto_schedule(4, 16, 80, 80, 64, 64, 64) == gla.SCHED_THREE_PHASE
+    assert gla.auto_schedule(1, 1, 4097, 16, 32, 32, 16) == gla.SCHED_THREE_PHASE
+    # more chains than the control words hold in one launch: three phases
+    assert gla.auto_schedule(1024, 64, 8, 8, 32, 32, 16) == gla.SCHED_THREE_PHASE
+    assert lib.gla_auto_schedule(1, 1, 4, 4, 48, 32, 16) == gla.E_UNSUPPORTED
+    assert lib.gla_auto_schedule(-1, 1, 4, 4, 32, 32, 16) == gla.E_ARG
