@@ -70,14 +70,19 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
   } while (0)
 
 // Auto dispatch: the single pass saves two kernel boundaries and one read of
-// k, v, gk, but every chunk reads O(sqrt(N)) published tiles; measured on
-// MI355X it is ahead up to 36 chunks per chain (any batch) and behind from
-// about 50 on, so chains longer than 36 chunks take the three phases.
-constexpr int kOnepassMaxChain = 36;
+// k, v, gk, but every chunk reads O(sqrt(N)) published tiles. Measured on
+// MI355X (64/64, chunk 64) it is ahead for chains of up to 32 chunks on grids
+// of up to a few thousand chunk-heads, and behind beyond either.
+constexpr int kOnepassMaxChain = 32;
+constexpr long kOnepassMaxChunks = 3072;
 
 bool single_pass_fits(const gla::Problem& p) {
   const int nb_max = p.B < gla::kMaxBatchPerLaunch ? p.B : gla::kMaxBatchPerLaunch;
   return gla::onepass_fits(p, nb_max);
+}
+
+bool prefer_single_pass(const gla::Problem& p) {
+  return p.N <= kOnepassMaxChain && (long)p.B * p.H * p.N <= kOnepassMaxChunks;
 }
 
 int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
@@ -105,7 +110,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
   GLA_TRY(check_ws(p, workspace, workspace_bytes));
   bool onepass = single_pass_fits(p);
   if (mode == 1 && !onepass) return GLA_E_UNSUPPORTED;
-  if (mode == 0) onepass = onepass && p.N <= kOnepassMaxChain;
+  if (mode == 0) onepass = onepass && prefer_single_pass(p);
   if (mode == 2) onepass = false;
   if (onepass) {
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -255,8 +260,8 @@ int gla_auto_schedule(int B, int H, int grid_h, int grid_w, int dk, int dv, int 
   bool empty;
   GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, GLA_F16, &p, &empty));
   if (empty) return GLA_SCHED_THREE_PHASE;
-  return single_pass_fits(p) && p.N <= kOnepassMaxChain ? GLA_SCHED_SINGLE_PASS
-                                                        : GLA_SCHED_THREE_PHASE;
+  return single_pass_fits(p) && prefer_single_pass(p) ? GLA_SCHED_SINGLE_PASS
+                                                       : GLA_SCHED_THREE_PHASE;
 }
 
 int gla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {

@@ -45,6 +45,16 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
+// Eight consecutive floats of an LDS row (16-byte aligned) in two reads.
+// Per-(sub-block, key dim) factors are fetched this way: eight scalar reads
+// under a wave-dependent condition would each be waited for in turn.
+__device__ __forceinline__ void lds8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
+  x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+}
+
 __device__ __forceinline__ floatx4 mfma16x16x16(half4 a, half4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
@@ -124,7 +134,8 @@ __global__ __launch_bounds__(kThreads, 8) void summary_kernel(
   constexpr int KU_BYTES = (VSTR > USTR ? VSTR : USTR) * DK * 2;
   __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
   __shared__ __attribute__((aligned(16))) char sKU[KU_BYTES];
-  __shared__ float sTot[NB][DK];
+  __shared__ __attribute__((aligned(16))) float sTot[NB][DK];
+  __shared__ __attribute__((aligned(16))) float sAft[NB][DK];  // totals of sub-blocks I..NB-1
   __shared__ int sRow[C];
   half_t (*sKh)[VSTR] = reinterpret_cast<half_t (*)[VSTR]>(sKU);
   half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sKU);
@@ -157,22 +168,23 @@ __global__ __launch_bounds__(kThreads, 8) void summary_kernel(
   __syncthreads();
 
   const long bhn = ((long)b * H + h) * N + n;
+  if (tid < NB * DK) {
+    const int I2 = tid / DK, d = tid % DK;
+    float aft = 0.f;
+    for (int J = I2; J < NB; ++J) aft += sTot[J][d];
+    sAft[I2][d] = aft;
+    if (I2 == 0) Aws[bhn * DK + d] = fexp2(aft);  // a = 2^B
+  }
+  __syncthreads();
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) {
-      const int d = 32 * (e / 8) + lk + (e % 8);
-      float rest = sTot[I][d] - sc[e];  // B - b_t, summed over later tokens
+    for (int ks = 0; ks < NKS; ++ks) {
+      float aft[8];
+      lds8(&sAft[I][32 * ks + lk], aft);
 #pragma unroll
-      for (int J = 0; J < NB; ++J)
-        if (J > I) rest += sTot[J][d];
-      sKh[d][t] = (half_t)(kf[e] * fexp2(rest));
+      for (int c = 0; c < 8; ++c)  // B - b_t: the decay of the later tokens
+        sKh[32 * ks + lk + c][t] = (half_t)(kf[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
     }
-  }
-  if (tid < DK) {
-    float B = 0.f;
-#pragma unroll
-    for (int J = 0; J < NB; ++J) B += sTot[J][tid];
-    Aws[bhn * DK + tid] = fexp2(B);
   }
   __syncthreads();
 
@@ -474,9 +486,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __shared__ __attribute__((aligned(16))) char sKO[KO_BYTES];
   __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
   __shared__ __attribute__((aligned(16))) char sX[X_BYTES];
-  __shared__ float sTot[NB][DK], sS7[NB][DK];
-  __shared__ float sEb[NB][DK], sR1[NB][DK], sR2[NB][DK];
-  __shared__ float sM[NPAIR > 0 ? NPAIR : 1][DK];
+  __shared__ __attribute__((aligned(16))) float sTot[NB][DK], sS7[NB][DK];
+  __shared__ __attribute__((aligned(16))) float sEb[NB][DK], sR1[NB][DK], sR2[NB][DK];
+  __shared__ __attribute__((aligned(16))) float sM[NPAIR > 0 ? NPAIR : 1][DK];
+  __shared__ __attribute__((aligned(16))) float sF[kFused ? NB : 1][DK];  // K^ = K~ * sF
   __shared__ float sAn[kFused ? DK : 1];
   __shared__ int sRow[C];
   __shared__ int sTier;
@@ -570,30 +583,30 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     if (!(range <= kF32Range)) atomicMax(&sTier, 2);
     else if (!(range <= kHalfRange)) atomicMax(&sTier, 1);
     if constexpr (kFused) {
+      float after = 0.f;  // totals of the later sub-blocks
+      for (int J = I2 + 1; J < NB; ++J) after += sTot[J][d];
+      sF[I2][d] = fexp2(after);
       if (I2 == NB - 1) sAn[d] = fexp2(beta + tot);  // a_n = 2^(chunk total)
     }
   }
+  __syncthreads();
   // -- per-element factors; K~ goes to LDS for the other sub-blocks, and in
   // one pass K^ = K~ 2^(totals of the later sub-blocks), transposed, for U
   float qt[NEL], kt[NEL];
   if (owner) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+      float tt[8], ff[8];
+      lds8(&sTot[I][32 * ks + lk], tt);
+      if constexpr (kFused) lds8(&sF[I][32 * ks + lk], ff);
       half8 k8;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int e = 8 * ks + c, d = 32 * ks + lk + c;
-        const float tot = sTot[I][d];
         qt[e] = qf[e] * fexp2(sc[e]);
-        kt[e] = kf[e] * fexp2(tot - sc[e]);
+        kt[e] = kf[e] * fexp2(tt[c] - sc[e]);
         k8[c] = (half_t)kt[e];
-        if constexpr (kFused) {
-          float rest = 0.f;
-#pragma unroll
-          for (int J = 0; J < NB; ++J)
-            if (J > I) rest += sTot[J][d];
-          sKh[d][t] = (half_t)(kt[e] * fexp2(rest));
-        }
+        if constexpr (kFused) sKh[d][t] = (half_t)(kt[e] * ff[c]);
       }
       *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = k8;
     }
@@ -653,21 +666,27 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     if (tier == 0) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
+        float r1[8], r2[8];
+        lds8(&sR1[I][32 * ks + lk], r1);
+        lds8(&sR2[I][32 * ks + lk], r2);
         half8 qa, ka;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const int e = 8 * ks + c, d = 32 * ks + lk + c;
-          qa[c] = (half_t)(qt[e] * sR1[I][d]);
-          ka[c] = (half_t)(kt[e] * sR2[I][d]);
+          qa[c] = (half_t)(qt[8 * ks + c] * r1[c]);
+          ka[c] = (half_t)(kt[8 * ks + c] * r2[c]);
         }
         dacc = mfma16x16x32(ka, qa, dacc);
       }
     } else if (tier == 1) {
 #pragma unroll
-      for (int e = 0; e < NEL; ++e) {
-        const int d = 32 * (e / 8) + lk + (e % 8);
-        dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[e] * sR2[I][d], qt[e] * sR1[I][d], dacc,
-                                                    0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        float r1[8], r2[8];
+        lds8(&sR1[I][32 * ks + lk], r1);
+        lds8(&sR2[I][32 * ks + lk], r2);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[8 * ks + c] * r2[c], qt[8 * ks + c] * r1[c],
+                                                      dacc, 0, 0, 0);
       }
     } else {
       // every entry directly: A_ij = sum_d q_i k_j 2^(s_i - s_j)
@@ -699,9 +718,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
+          float mm[8];
+          lds8(&sM[pr][32 * ks + lk], mm);
           half8 qm;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) qm[c] = (half_t)(qt[8 * ks + c] * sM[pr][32 * ks + lk + c]);
+          for (int c = 0; c < 8; ++c) qm[c] = (half_t)(qt[8 * ks + c] * mm[c]);
           const half8 ka = *reinterpret_cast<const half8*>(&sKt[16 * J + lr][32 * ks + lk]);
           acc = mfma16x16x32(ka, qm, acc);
         }
@@ -710,9 +731,12 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < NKS; ++ks) {
+      float eb[8];
+      lds8(&sEb[I][32 * ks + lk], eb);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) qh[ks][c] = (half_t)(qt[8 * ks + c] * sEb[I][32 * ks + lk + c]);
+      for (int c = 0; c < 8; ++c) qh[ks][c] = (half_t)(qt[8 * ks + c] * eb[c]);
+    }
   }
 
   if constexpr (!kFused) {
