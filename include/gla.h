@@ -199,6 +199,25 @@ int gla_chunk_outputs(const void* q, const void* k, const void* v,
 int gla_scan_perm(int32_t* perm_dev, int grid_h, int grid_w, int dir,
                   void* stream);
 
+/* Spatial SwiGLU core: the channel mixer of a GTR block (ai.info summary of
+ * GTR, "Methodology in Plain English"; project page, "How GTR Works") puts a
+ * 3x3 depthwise convolution, on the 2-D patch grid, into the value branch of
+ * a SwiGLU block. With the input projections already applied by the caller,
+ * a (gate branch) and u (value branch), this computes for every token (y, x)
+ * of the grid and channel c
+ *   h[y][x][c] = silu(a[y][x][c]) * (bias[c] +
+ *                 sum_{i,j=0..2} weight[c][i][j] * u[y+i-1][x+j-1][c])
+ * with u taken as zero outside the grid and silu(z) = z / (1 + exp(-z)).
+ *   a, u, h : [B][T][F] device memory, raster token order (token = y*grid_w+x),
+ *             IEEE half (GLA_F16) or float (GLA_F32); 16-byte aligned;
+ *             h must not be the same buffer as a or u.
+ *   weight  : float [F][3][3] device memory; bias: float [F] or NULL.
+ * F must be a multiple of 8 (GLA_E_UNSUPPORTED otherwise). Accumulation is
+ * float. Asynchronous on `stream`; allocates nothing. */
+int gla_spatial_swiglu(const void* a, const void* u, const float* weight,
+                       const float* bias, void* h, int B, int grid_h,
+                       int grid_w, int F, int dtype, void* stream);
+
 /* Static text for a status code; never NULL. */
 const char* gla_status_string(int status);
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgla_mi355x.so")
-SOURCES = ["gla_kernels.hip", "gla_api.hip"]
+SOURCES = ["gla_kernels.hip", "ssw_kernels.hip", "gla_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -286,6 +286,25 @@ int gla_scan_perm(int32_t* perm_dev, int grid_h, int grid_w, int dir, void* stre
   return GLA_OK;
 }
 
+int gla_spatial_swiglu(const void* a, const void* u, const float* weight, const float* bias,
+                       void* h, int B, int grid_h, int grid_w, int F, int dtype, void* stream) {
+  if (B < 0 || grid_h < 0 || grid_w < 0 || F < 0) return GLA_E_ARG;
+  if (dtype != GLA_F16 && dtype != GLA_F32) return GLA_E_ARG;
+  if (F % 8 != 0) return GLA_E_UNSUPPORTED;
+  const long long T = (long long)grid_h * grid_w;
+  if (T > 0x7fffffffLL || (long long)B * T * F > (1LL << 40) || B > 65535) return GLA_E_UNSUPPORTED;
+  if (B == 0 || T == 0 || F == 0) return GLA_OK;
+  GLA_TRY(check_tensor(a));
+  GLA_TRY(check_tensor(u));
+  GLA_TRY(check_tensor(h));
+  if (!weight || !aligned(weight, 4) || (bias && !aligned(bias, 4))) return GLA_E_ARG;
+  if (h == a || h == u) return GLA_E_ARG;
+  const hipError_t e = gla::launch_spatial_swiglu(dtype, a, u, weight, bias, h, B, grid_h, grid_w,
+                                                  F, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "spatial swiglu launch");
+  return GLA_OK;
+}
+
 const char* gla_status_string(int status) {
   switch (status) {
     case GLA_OK: return "GLA_OK";

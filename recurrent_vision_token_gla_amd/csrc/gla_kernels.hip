@@ -123,7 +123,7 @@ __device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT,
 // staged through LDS as rows of key dims and stored as half [dk][dv].
 // ===========================================================================
 template <int DK, int DV, int C, typename InT>
-__global__ __launch_bounds__(kThreads, 8) void summary_kernel(
+__global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     const InT* __restrict__ kp, const InT* __restrict__ vp, const InT* __restrict__ gp,
     half_t* __restrict__ Uws, float* __restrict__ Aws, int T, int H, int N, int gh, int gw,
     DirPack dirs) {

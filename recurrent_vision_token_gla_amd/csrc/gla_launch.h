@@ -50,6 +50,10 @@ hipError_t launch_onepass(const Problem& p, int b0, int nb, const DirPack& dirs,
                           const float* s0, float* sfin, hipStream_t s);
 // Zero the control words of a workspace (a fill kernel, graph-capturable).
 hipError_t launch_ctrl_clear(char* ws, hipStream_t s);
+// Spatial SwiGLU core (ssw_kernels.hip): h = silu(a) * (3x3 depthwise conv of u + bias).
+hipError_t launch_spatial_swiglu(int dtype, const void* a, const void* u, const float* w,
+                                 const float* bias, void* h, int B, int gh, int gw, int F,
+                                 hipStream_t s);
 hipError_t launch_scan_perm(int32_t* perm, int gh, int gw, int dir, hipStream_t s);
 
 }  // namespace gla

@@ -23,7 +23,7 @@ OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 # every symbol declared in include/gla.h
 EXPORTS = ["gla_abi_version", "gla_fwd_workspace_bytes", "gla_workspace_layout", "gla_fwd",
            "gla_fwd_state", "gla_fwd_schedule", "gla_auto_schedule", "gla_workspace_init",
-           "gla_chunk_summaries", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
+           "gla_chunk_summaries", "gla_spatial_swiglu", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
            "gla_status_string", "gla_last_error_detail"]
 
 _lib = None
@@ -74,6 +74,8 @@ def load():
     lib.gla_chunk_outputs.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
     lib.gla_scan_perm.restype = _i32
     lib.gla_scan_perm.argtypes = [_vp, _i32, _i32, _i32, _vp]
+    lib.gla_spatial_swiglu.restype = _i32
+    lib.gla_spatial_swiglu.argtypes = [_vp] * 5 + [_i32] * 5 + [_vp]
     lib.gla_status_string.restype = ctypes.c_char_p
     lib.gla_status_string.argtypes = [_i32]
     lib.gla_last_error_detail.restype = ctypes.c_char_p
@@ -279,3 +281,31 @@ def scan_perm(grid_h: int, grid_w: int, direction: int, device="cuda", stream=No
     st = load().gla_scan_perm(perm.data_ptr(), grid_h, grid_w, direction, _stream_ptr(stream))
     _check(st, "gla_scan_perm")
     return perm[:grid_h * grid_w]
+
+
+def spatial_swiglu(a: torch.Tensor, u: torch.Tensor, weight: torch.Tensor,
+                   bias: Optional[torch.Tensor], grid_h: int, grid_w: int,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """h = silu(a) * (3x3 depthwise conv of u on the grid + bias); a, u [B, T, F]
+    (float16 or float32, contiguous), weight [F, 3, 3] and bias [F] float32."""
+    for name, t in (("a", a), ("u", u)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous [B, T, F] device tensor")
+    if a.shape != u.shape or a.dtype != u.dtype:
+        raise ValueError("a and u must share shape and dtype")
+    B, T, Fc = u.shape
+    if T != grid_h * grid_w:
+        raise ValueError(f"T={T} but grid is {grid_h}x{grid_w}")
+    if weight.dtype != torch.float32 or tuple(weight.shape) != (Fc, 3, 3) or \
+            not weight.is_contiguous() or not weight.is_cuda:
+        raise ValueError("weight must be a contiguous float32 [F, 3, 3] device tensor")
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (Fc,)
+                             or not bias.is_cuda):
+        raise ValueError("bias must be a float32 [F] device tensor")
+    if out is None:
+        out = torch.empty_like(u)
+    st = load().gla_spatial_swiglu(a.data_ptr(), u.data_ptr(), weight.data_ptr(),
+                                   None if bias is None else bias.data_ptr(), out.data_ptr(),
+                                   B, grid_h, grid_w, Fc, _dtype_code(u), _stream_ptr(stream))
+    _check(st, "gla_spatial_swiglu")
+    return out

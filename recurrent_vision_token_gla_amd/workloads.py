@@ -133,3 +133,55 @@ def workload_inputs(w: Workload, call: int):
     return make_inputs(w.B, w.T, w.H, w.dk, w.dv, w.np_dtype,
                        seed_for(w.index, call), gate=w.gate)
 
+
+
+# ---------------------------------------------------------------------------
+# Block epilogue and channel-mixer inputs. The pages give no widths for the
+# channel mixer; SSW_WORKLOADS use F = 2048, the SwiGLU hidden width of a
+# 768-wide block at the usual 8/3 ratio, on the same 40x40 and 80x80 grids.
+# Draws (all standard normal unless stated): output-gate rows z; RMSNorm
+# weight 1 + 0.1 N(0,1); gate branch a; value branch u; depthwise weights
+# N(0,1)/3 (fan-in 9); bias 0.1 N(0,1).
+
+@dataclasses.dataclass(frozen=True)
+class SswWorkload:
+    name: str
+    B: int
+    grid_h: int
+    grid_w: int
+    F: int
+    dtype: str = "f16"
+
+    @property
+    def T(self) -> int:
+        return self.grid_h * self.grid_w
+
+
+SSW_WORKLOADS = [
+    SswWorkload("ssw_img640_40x40_f2048", B=1, grid_h=40, grid_w=40, F=2048),
+    SswWorkload("ssw_img1280_80x80_f2048", B=1, grid_h=80, grid_w=80, F=2048),
+]
+
+GATE_EPS = 1e-6
+
+
+def make_gate_inputs(B: int, T: int, H: int, dv: int, dtype, seed: int):
+    """Output-gate rows z [B, T, H, dv] in `dtype` and the RMSNorm weight
+    [dv] in float32."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((B, T, H, dv))
+    w = 1.0 + 0.1 * rng.standard_normal(dv)
+    return np.ascontiguousarray(z.astype(dtype)), np.ascontiguousarray(w.astype(np.float32))
+
+
+def make_ssw_inputs(B: int, T: int, F: int, dtype, seed: int, with_bias: bool = True):
+    """a, u [B, T, F] in `dtype`; weight [F, 3, 3] and bias [F] (or None) in
+    float32."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((B, T, F))
+    u = rng.standard_normal((B, T, F))
+    w = rng.standard_normal((F, 3, 3)) / 3.0
+    bias = 0.1 * rng.standard_normal(F) if with_bias else None
+    cast = lambda x: np.ascontiguousarray(x.astype(dtype))
+    return (cast(a), cast(u), np.ascontiguousarray(w.astype(np.float32)),
+            None if bias is None else np.ascontiguousarray(bias.astype(np.float32)))
