@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "chunkwise GLA fwd tokens/s (fp16) at 1600/6400 tokens; % of roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_SOURCES = ["gla_kernels.hip", "gla_device.h", "gla_launch.h"]
+KERNEL_SOURCES = ["gla_kernels.hip", "gla_chunk.h", "gla_tile.h", "gla_gated.hip",
+                  "ssw_kernels.hip", "gla_device.h", "gla_launch.h"]
 
 
 def source_sha() -> str:

@@ -144,6 +144,22 @@ int gla_fwd_state(const void* q, const void* k, const void* v, const void* gk,
                   float* s_final, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* The forward with the GLA block's output gate fused into the store (ai.info
+ * summary of GTR, "Methodology in Plain English": a data-dependent output
+ * gate applied to the RMS-normalised output). Per (batch, token, head) row:
+ *   y = o / sqrt(mean_e(o_e^2) + eps) * norm_weight * silu(gate),
+ *   silu(z) = z / (1 + exp(-z)),
+ * with o the forward of gla_fwd_state (same s0 / s_final semantics), which is
+ * not written itself. gate: [B][T][H][dv] in the input dtype (16-byte
+ * aligned, not the same buffer as y); norm_weight: float [dv] (16-byte
+ * aligned), shared by the heads; eps >= 0. Same schedules as gla_fwd. */
+int gla_fwd_gated(const void* q, const void* k, const void* v, const void* gk,
+                  const void* gate, const float* norm_weight, float eps, void* y,
+                  int B, int H, int grid_h, int grid_w, int dk, int dv,
+                  const int32_t* dir, int chunk, int dtype, const float* s0,
+                  float* s_final, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* gla_fwd_state with an explicit schedule: GLA_SCHED_AUTO (what gla_fwd and
  * gla_fwd_state do), GLA_SCHED_SINGLE_PASS (returns GLA_E_UNSUPPORTED if the
  * problem does not fit its control words: more than 4096 chunks per chain,

@@ -85,10 +85,37 @@ bool prefer_single_pass(const gla::Problem& p) {
   return p.N <= kOnepassMaxChain && (long)p.B * p.H * p.N <= kOnepassMaxChunks;
 }
 
+int outputs_impl(const void* q, const void* k, const void* v, const void* gk, void* o, int B,
+                 int H, int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk,
+                 int dtype, void* workspace, size_t workspace_bytes, const gla::Epilogue& epi,
+                 void* stream) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
+  if (empty) return GLA_OK;
+  GLA_TRY(check_tensor(q));
+  GLA_TRY(check_tensor(k));
+  GLA_TRY(check_tensor(v));
+  GLA_TRY(check_tensor(gk));
+  GLA_TRY(check_tensor(o));
+  if (o == q || o == k || o == v || o == gk) return GLA_E_ARG;
+  GLA_TRY(check_dirs(dir, B));
+  GLA_TRY(check_ws(p, workspace, workspace_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
+    const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
+    const hipError_t e = gla::launch_outputs(p, b0, nb, pack_dirs(dir, b0, nb), q, k, v, gk,
+                                             o, static_cast<const char*>(workspace), epi, s);
+    if (e != hipSuccess) return fail_hip(e, "chunk outputs launch");
+  }
+  return GLA_OK;
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
              int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
              const float* s0, float* s_final, void* workspace, size_t workspace_bytes,
-             void* stream, int mode /* 0 auto, 1 single pass, 2 three phases */) {
+             void* stream, int mode /* 0 auto, 1 single pass, 2 three phases */,
+             const gla::Epilogue& epi = gla::Epilogue()) {
   gla::Problem p;
   bool empty;
   GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
@@ -106,6 +133,11 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
     const void* sf = s_final;
     if (sf == q || sf == k || sf == v || sf == gk || sf == o || sf == workspace) return GLA_E_ARG;
   }
+  if (epi.gate) {
+    GLA_TRY(check_tensor(epi.gate));
+    if (!epi.weight || !aligned(epi.weight, 16)) return GLA_E_ARG;
+    if (o == epi.gate || !(epi.eps >= 0.f)) return GLA_E_ARG;
+  }
   GLA_TRY(check_dirs(dir, B));
   GLA_TRY(check_ws(p, workspace, workspace_bytes));
   bool onepass = single_pass_fits(p);
@@ -117,7 +149,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
     for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
       const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
       const hipError_t e = gla::launch_onepass(p, b0, nb, pack_dirs(dir, b0, nb), q, k, v, gk, o,
-                                               static_cast<char*>(workspace), s0, s_final, s);
+                                               static_cast<char*>(workspace), s0, s_final, epi, s);
       if (e != hipSuccess) return fail_hip(e, "single-pass launch");
     }
     return GLA_OK;
@@ -126,15 +158,15 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
                               workspace, workspace_bytes, stream));
   GLA_TRY(gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, s0, s_final, workspace,
                          workspace_bytes, stream));
-  return gla_chunk_outputs(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype,
-                           workspace, workspace_bytes, stream);
+  return outputs_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, workspace,
+                      workspace_bytes, epi, stream);
 }
 
 }  // namespace
 
 extern "C" {
 
-int gla_abi_version(void) { return 3; }
+int gla_abi_version(void) { return 4; }
 
 size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv,
                                int chunk) {
@@ -207,26 +239,8 @@ int gla_chunk_outputs(const void* q, const void* k, const void* v, const void* g
                       int B, int H, int grid_h, int grid_w, int dk, int dv,
                       const int32_t* dir, int chunk, int dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  gla::Problem p;
-  bool empty;
-  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
-  if (empty) return GLA_OK;
-  GLA_TRY(check_tensor(q));
-  GLA_TRY(check_tensor(k));
-  GLA_TRY(check_tensor(v));
-  GLA_TRY(check_tensor(gk));
-  GLA_TRY(check_tensor(o));
-  if (o == q || o == k || o == v || o == gk) return GLA_E_ARG;
-  GLA_TRY(check_dirs(dir, B));
-  GLA_TRY(check_ws(p, workspace, workspace_bytes));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
-    const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
-    const hipError_t e = gla::launch_outputs(p, b0, nb, pack_dirs(dir, b0, nb), q, k, v, gk,
-                                             o, static_cast<const char*>(workspace), s);
-    if (e != hipSuccess) return fail_hip(e, "chunk outputs launch");
-  }
-  return GLA_OK;
+  return outputs_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, workspace,
+                      workspace_bytes, gla::Epilogue(), stream);
 }
 
 int gla_fwd(const void* q, const void* k, const void* v, const void* gk, void* o, int B, int H,
@@ -253,6 +267,20 @@ int gla_fwd_schedule(const void* q, const void* k, const void* v, const void* gk
     return GLA_E_ARG;
   return fwd_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, s0, s_final,
                   workspace, workspace_bytes, stream, schedule);
+}
+
+int gla_fwd_gated(const void* q, const void* k, const void* v, const void* gk, const void* gate,
+                  const float* norm_weight, float eps, void* y, int B, int H, int grid_h,
+                  int grid_w, int dk, int dv, const int32_t* dir, int chunk, int dtype,
+                  const float* s0, float* s_final, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  gla::Epilogue epi;
+  epi.gate = gate;
+  epi.weight = norm_weight;
+  epi.eps = eps;
+  if (!gate) return GLA_E_ARG;
+  return fwd_impl(q, k, v, gk, y, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, s0, s_final,
+                  workspace, workspace_bytes, stream, 0, epi);
 }
 
 int gla_auto_schedule(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk) {

@@ -41,13 +41,29 @@ hipError_t launch_summaries(const Problem& p, int b0, int nb, const DirPack& dir
 // s0 / sfin (nullable) are the full-problem [B][H][dk][dv] fp32 state arrays.
 hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* s0,
                        float* sfin, hipStream_t s);
+// Optional fused epilogue of the chunk kernels: with gate != nullptr the
+// output rows become o / sqrt(mean(o^2) + eps) * weight * silu(gate) (gate
+// [B][T][H][dv] in the input dtype, weight float [dv]).
+struct Epilogue {
+  const void* gate = nullptr;
+  const float* weight = nullptr;
+  float eps = 0.f;
+};
+
 hipError_t launch_outputs(const Problem& p, int b0, int nb, const DirPack& dirs,
                           const void* q, const void* k, const void* v, const void* gk,
-                          void* o, const char* ws, hipStream_t s);
+                          void* o, const char* ws, const Epilogue& epi, hipStream_t s);
+hipError_t launch_outputs_gated(const Problem& p, int b0, int nb, const DirPack& dirs,
+                                const void* q, const void* k, const void* v, const void* gk,
+                                void* o, const char* ws, const Epilogue& epi, hipStream_t s);
 // The whole forward in one kernel (requires onepass_fits(p, nb)).
 hipError_t launch_onepass(const Problem& p, int b0, int nb, const DirPack& dirs, const void* q,
                           const void* k, const void* v, const void* gk, void* o, char* ws,
-                          const float* s0, float* sfin, hipStream_t s);
+                          const float* s0, float* sfin, const Epilogue& epi, hipStream_t s);
+hipError_t launch_onepass_gated(const Problem& p, int b0, int nb, const DirPack& dirs,
+                                const void* q, const void* k, const void* v, const void* gk,
+                                void* o, char* ws, const float* s0, float* sfin,
+                                const Epilogue& epi, hipStream_t s);
 // Zero the control words of a workspace (a fill kernel, graph-capturable).
 hipError_t launch_ctrl_clear(char* ws, hipStream_t s);
 // Spatial SwiGLU core (ssw_kernels.hip): h = silu(a) * (3x3 depthwise conv of u + bias).

@@ -1,0 +1,179 @@
+// Device helpers shared by the forward's kernels: exp2, DPP row scans,
+// matrix-core wrappers, LDS row reads, the chunk's token rows in scan order,
+// and the coherent publish / wait primitives of the single-pass schedule.
+#pragma once
+
+#include "gla_device.h"
+
+namespace gla {
+namespace tile {
+
+// exp2 on the transcendental unit. Results below 2^-126 flush to zero; every
+// factor built with it multiplies a term that is then negligible.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float row_scan16(float x) {
+  // inclusive prefix sum over the 16 lanes of each DPP row
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+  return x;
+}
+
+// Eight consecutive floats of an LDS row (16-byte aligned) in two reads.
+// Per-(sub-block, key dim) factors are fetched this way: eight scalar reads
+// under a wave-dependent condition would each be waited for in turn.
+__device__ __forceinline__ void lds8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
+  x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+}
+
+__device__ __forceinline__ floatx4 mfma16x16x16(half4 a, half4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Raster row of every token of the chunk (-1 past the end of the sequence).
+template <int C>
+__device__ __forceinline__ void chunk_rows(int* sRow, int tok0, int T, int gh, int gw, int dir) {
+  const int tid = threadIdx.x;
+  const int L = min(C, T - tok0);
+  if (tid < C) sRow[tid] = tid < L ? scan_to_raster(tok0 + tid, T, gh, gw, dir) : -1;
+}
+
+// Token row t of a [B][T][H][D] tensor, this lane's 8*NKS dims
+// d = 32*ks + lk + c, in float (zero for padding rows). The loads are
+// unconditional (a padding row reads row 0 and is zeroed afterwards): a load
+// under a divergent branch would be waited for before the branches rejoin,
+// which would serialize every load of the kernel's prologue.
+template <int D, int NKS, typename InT>
+__device__ __forceinline__ void load_row(const InT* p, long row, int lk, float* x) {
+  const bool valid = row >= 0;
+  const InT* r = p + (valid ? row : 0) * D + lk;
+  float y[NKS][8];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) load8(r + 32 * ks, y[ks]);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[8 * ks + c] = valid ? y[ks][c] : 0.f;
+}
+
+// V rows of the chunk, transposed into sVt[e][token] (half); loads
+// unconditional as in load_row.
+template <int DV, int C, int VSTR, typename InT>
+__device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT, int H, int h,
+                                        half_t (*sVt)[VSTR]) {
+  constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
+  half8 v8[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int u = threadIdx.x + kThreads * it;
+    const int r = (u / (DV / 8)) % C, c8 = (u % (DV / 8)) * 8;
+    const int row = sRow[r] >= 0 ? sRow[r] : 0;
+    v8[it] = load8h(vp + ((bT + row) * H + h) * DV + c8);
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int u = threadIdx.x + kThreads * it;
+    const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
+    if (u < C * (DV / 8)) {
+      const bool valid = sRow[r] >= 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sVt[c8 + c][r] = valid ? v8[it][c] : (half_t)0.f;
+    }
+  }
+}
+
+__device__ __forceinline__ void load_f8(const float* p, float (&a)[8]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  const float4 y = *reinterpret_cast<const float4*>(p + 4);
+  a[0] = x.x, a[1] = x.y, a[2] = x.z, a[3] = x.w;
+  a[4] = y.x, a[5] = y.y, a[6] = y.z, a[7] = y.w;
+}
+
+__device__ __forceinline__ void store_f8(float* p, const float (&a)[8]) {
+  *reinterpret_cast<float4*>(p) = float4{a[0], a[1], a[2], a[3]};
+  *reinterpret_cast<float4*>(p + 4) = float4{a[4], a[5], a[6], a[7]};
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_shr(float x, float fill) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// ===========================================================================
+// Single-pass schedule: control words at the start of the workspace.
+//   word 0            sticky error bits (kErrSpin: a bounded wait ran out)
+//   per chain c (one (batch, head) of a launch), kCtrlHeader + c*(N+nseg+1):
+//     [0, N)          chunk n has published U_n and a_n
+//     [N, N+nseg)     segment s has published its aggregate
+//     [N+nseg]        chunks of the chain that have finished reading
+// All of them are zero between calls: the last chunk of a chain to finish
+// reading clears the chain's words, so a workspace zeroed once stays valid.
+// ===========================================================================
+constexpr unsigned kErrSpin = 1u;
+constexpr long kSpinLimit = 1L << 21;  // polls of one wait (seconds, far above any real wait)
+
+// Data one workgroup publishes for others in the same kernel (summaries, their
+// decays, segment aggregates) is written and read only with device-scope
+// atomic accesses (relaxed, 8 or 4 bytes). Those are coherent across the
+// XCDs' L2 caches by themselves, so publishing needs no L2 write-back and
+// reading no L2 invalidation, which would cost every workgroup on the XCD:
+//   publisher: coherent stores; each wave waits for their completion;
+//              barrier; one flag store.
+//   reader:    one wave polls the flags; barrier; coherent loads.
+typedef unsigned long u64x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void st_dev(half_t* p, half8 v) {
+  const u64x2 w = __builtin_bit_cast(u64x2, v);
+  unsigned long* q = reinterpret_cast<unsigned long*>(p);
+  __hip_atomic_store(q, w.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, w.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ half8 ld_dev(const half_t* p) {
+  const unsigned long* q = reinterpret_cast<const unsigned long*>(p);
+  u64x2 w;
+  w.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  w.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(half8, w);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lane i of the calling wave watches flags[i], i < count <= 64. Returns once
+// every watched flag is set, or when the poll budget runs out (recorded in
+// *err). The caller then passes a workgroup barrier before reading.
+__device__ __forceinline__ void wave_wait_flags(const unsigned* flags, int count, unsigned* err) {
+  const int lane = threadIdx.x & 63;
+  if (count <= 0) return;
+  for (long it = 0;; ++it) {
+    bool ok = true;
+    if (lane < count)
+      ok = __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    if (__all(ok)) break;
+    if (it >= kSpinLimit) {
+      if (lane == 0) atomicOr(err, kErrSpin);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Every wave waits until its coherent stores have completed, then one flag
+// is set. Must be reached by the whole workgroup.
+__device__ __forceinline__ void publish(unsigned* flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace tile
+}  // namespace gla

@@ -22,7 +22,7 @@ OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 # every symbol declared in include/gla.h
 EXPORTS = ["gla_abi_version", "gla_fwd_workspace_bytes", "gla_workspace_layout", "gla_fwd",
-           "gla_fwd_state", "gla_fwd_schedule", "gla_auto_schedule", "gla_workspace_init",
+           "gla_fwd_state", "gla_fwd_gated", "gla_fwd_schedule", "gla_auto_schedule", "gla_workspace_init",
            "gla_chunk_summaries", "gla_spatial_swiglu", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
            "gla_status_string", "gla_last_error_detail"]
 
@@ -59,6 +59,9 @@ def load():
     lib.gla_fwd_state.restype = _i32
     lib.gla_fwd_state.argtypes = ([_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _vp, _vp, _sz,
                                                             _vp])
+    lib.gla_fwd_gated.restype = _i32
+    lib.gla_fwd_gated.argtypes = ([_vp] * 6 + [ctypes.c_float, _vp] + [_i32] * 6 +
+                                  [_i32p, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
     lib.gla_fwd_schedule.restype = _i32
     lib.gla_fwd_schedule.argtypes = ([_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _vp, _i32,
                                                                _vp, _sz, _vp])
@@ -226,6 +229,36 @@ def fwd_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tenso
                                  workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
     _check(st, "gla_fwd_schedule")
     return (out, s_final) if return_state else out
+
+
+def fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
+              gate: torch.Tensor, norm_weight: torch.Tensor, eps: float, grid_h: int,
+              grid_w: int, direction: Union[int, Sequence[int]] = L2R, chunk: int = 64,
+              s0: Optional[torch.Tensor] = None, s_final: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """y = RMSNorm(o) * norm_weight * silu(gate) with o the forward (from s0,
+    None for zero; S_T into s_final if given); gate [B, T, H, dv] in q's
+    dtype, norm_weight [dv] float32."""
+    B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
+    if gate.shape != v.shape or gate.dtype != q.dtype or not gate.is_contiguous() or \
+            not gate.is_cuda:
+        raise ValueError("gate must be a contiguous device tensor shaped like v, in q's dtype")
+    if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (dv,) or \
+            not norm_weight.is_cuda or not norm_weight.is_contiguous():
+        raise ValueError("norm_weight must be a contiguous float32 [dv] device tensor")
+    if out is None:
+        out = torch.empty_like(v)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
+    st = load().gla_fwd_gated(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                              gate.data_ptr(), norm_weight.data_ptr(), float(eps),
+                              out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
+                              chunk, _dtype_code(q), _state_ptr(s0, B, H, dk, dv, "s0"),
+                              _state_ptr(s_final, B, H, dk, dv, "s_final"), workspace.data_ptr(),
+                              workspace.numel(), _stream_ptr(stream))
+    _check(st, "gla_fwd_gated")
+    return out
 
 
 def chunk_summaries(k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspace=None,

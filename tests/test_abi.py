@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gla_abi_version() == 3
+    assert lib.gla_abi_version() == 4
     for st in (0, -1, -2, -3, -4, 7):
         s = lib.gla_status_string(st)
         assert s and isinstance(s, bytes)
@@ -170,3 +170,19 @@ def test_auto_schedule(lib):
     assert gla.auto_schedule(1024, 64, 8, 8, 32, 32, 16) == gla.SCHED_THREE_PHASE
     assert lib.gla_auto_schedule(1, 1, 4, 4, 48, 32, 16) == gla.E_UNSUPPORTED
     assert lib.gla_auto_schedule(-1, 1, 4, 4, 32, 32, 16) == gla.E_ARG
+
+
+def test_gated_forward_validates(lib):
+    arr = (ctypes.c_int32 * 1)(0)
+
+    def gated(gate=FAKE + 0x6000, w=FAKE + 0x7000, eps=1e-6, y=FAKE + 0x4000):
+        return lib.gla_fwd_gated(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, gate, w,
+                                 ctypes.c_float(eps), y, 1, 1, 4, 4, 32, 32, arr, 16, 0, None,
+                                 None, FAKE + 0x5000, 10 ** 6, None)
+    assert gated(gate=None) == gla.E_ARG
+    assert gated(gate=FAKE + 0x6008) == gla.E_ARG     # misaligned gate
+    assert gated(w=None) == gla.E_ARG
+    assert gated(w=FAKE + 0x7004) == gla.E_ARG        # misaligned weight
+    assert gated(eps=-1.0) == gla.E_ARG
+    assert gated(y=FAKE + 0x6000) == gla.E_ARG        # output is the gate buffer
+    assert gated(y=FAKE) == gla.E_ARG                 # output is q
