@@ -201,6 +201,89 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
                 schedule="single_pass" if sched == gla.SCHED_SINGLE_PASS else "three_phase")
 
 
+def time_graph(torch, fn, reps=20, rounds=5):
+    """Median microseconds per call of fn, from `reps` calls captured back to
+    back in one graph and replayed `rounds` times (events on the launching
+    stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(rounds):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / reps)
+    return statistics.median(ts)
+
+
+def token_sweep(torch, gla, W, np):
+    """Self-relative scaling over the pages' token counts (16x16, 40x40, 80x80
+    and 128x128 grids: 256, 1.6K, 6.4K, 16.4K tokens) for the configs' head
+    shape (64/64) and the pages' operator shape (dk 32, dv 64); B 1, H 6,
+    chunk 64, direction left->right, auto schedule."""
+    out = []
+    for dk, dv in ((64, 64), (32, 64)):
+        for g in (16, 40, 80, 128):
+            T = g * g
+            q, k, v, gk = W.make_inputs(1, T, 6, dk, dv, np.float16, seed=7000 + g + dk)
+            tq, tk, tv, tg = (torch.from_numpy(x).cuda() for x in (q, k, v, gk))
+            ws = gla.alloc_workspace(1, 6, g, g, dk, dv, 64)
+            o = torch.empty_like(tv)
+            us = time_graph(torch, lambda s: gla.fwd(tq, tk, tv, tg, g, g, [0], 64, out=o,
+                                                     workspace=ws, stream=s))
+            nbytes = T * 6 * (3 * dk + 2 * dv) * 2
+            out.append({"dk": dk, "dv": dv, "grid": f"{g}x{g}", "tokens": T, "us_per_call": us,
+                        "tokens_per_s": T / (us * 1e-6),
+                        "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "schedule": "single_pass" if gla.auto_schedule(1, 6, g, g, dk, dv, 64)
+                        == gla.SCHED_SINGLE_PASS else "three_phase"})
+    return out
+
+
+def extra_kernels(torch, gla, W, np):
+    """The fused output gate at the 640^2 shape and the Spatial SwiGLU core on
+    its two workloads, each with its own HBM roofline fraction."""
+    res = {}
+    wl = W.WORKLOADS[1]
+    q, k, v, gk = W.workload_inputs(wl, 0)
+    z, wn = W.make_gate_inputs(wl.B, wl.T, wl.H, wl.dv, np.float16, seed=7100)
+    tq, tk, tv, tg, tz = (torch.from_numpy(x).cuda() for x in (q, k, v, gk, z))
+    tw = torch.from_numpy(wn).cuda()
+    ws = gla.alloc_workspace(wl.B, wl.H, wl.grid_h, wl.grid_w, wl.dk, wl.dv, wl.chunk)
+    y = torch.empty_like(tv)
+    us = time_graph(torch, lambda s: gla.fwd_gated(tq, tk, tv, tg, tz, tw, W.GATE_EPS, wl.grid_h,
+                                                   wl.grid_w, [0], wl.chunk, out=y, workspace=ws,
+                                                   stream=s))
+    nbytes = wl.T * wl.H * (3 * wl.dk + 3 * wl.dv) * 2  # + the gate rows
+    res["gated_" + wl.name] = {"us_per_call": us, "tokens_per_s": wl.T / (us * 1e-6),
+                               "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    for sw in W.SSW_WORKLOADS:
+        a, u, w, bias = W.make_ssw_inputs(sw.B, sw.T, sw.F, np.float16, seed=7200)
+        ta, tu, tw2, tb = (torch.from_numpy(x).cuda() for x in (a, u, w, bias))
+        h = torch.empty_like(tu)
+        us = time_graph(torch, lambda s: gla.spatial_swiglu(ta, tu, tw2, tb, sw.grid_h, sw.grid_w,
+                                                            out=h, stream=s))
+        nbytes = sw.B * sw.T * sw.F * 2 * 3 + sw.F * 40  # a, u, h + weights and bias
+        res[sw.name] = {"us_per_call": us, "tokens_per_s": sw.B * sw.T / (us * 1e-6),
+                        "achieved_GBs": nbytes / (us * 1e-6) / 1e9,
+                        "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def parity_check(w, res, oracle, np, max_bh=4):
     """Max relative error of the benchmarked outputs against the oracle, on
     a sample of (batch, head) slices of every call."""
@@ -346,6 +429,18 @@ def main():
         del ri
         torch.cuda.empty_cache()
 
+    sweep = extras = None
+    if not args.no_also:
+        sweep = token_sweep(torch, gla, W, np)
+        for r in sweep:
+            print(f"# sweep dk{r['dk']}/dv{r['dv']} {r['grid']}: {r['us_per_call']:.2f} us, "
+                  f"{r['tokens_per_s']:.3g} tokens/s, {100 * r['hbm_frac']:.1f}% HBM, "
+                  f"{r['schedule']}", file=sys.stderr, flush=True)
+        extras = extra_kernels(torch, gla, W, np)
+        for k2, r in extras.items():
+            print(f"# {k2}: {r['us_per_call']:.2f} us, {100 * r['hbm_frac']:.1f}% HBM",
+                  file=sys.stderr, flush=True)
+
     line = {
         "metric": METRIC,
         "value": s["value"],
@@ -371,6 +466,8 @@ def main():
         "parity_max_rel_err": parity,
         "cpu_baseline": cpu,
         "also": also,
+        "sweep": sweep,
+        "extras": extras,
         "kernel_source_sha": source_sha(),
     }
     print(json.dumps(line), flush=True)
