@@ -47,7 +47,7 @@
  * segments, whose last chunks publish segment aggregates), and adds the
  * readout. Workgroups run in chain-major order and only wait on earlier
  * ones, with bounded waits. gla_fwd picks the single pass for chains of at
- * most 32 chunks on grids of at most 3072 chunk-heads (if the launch fits
+ * most 32 chunks on grids of at most 1024 chunk-heads (if the launch fits
  * its control words), and the three phases otherwise.
  *
  * Workspace: caller-owned device memory of gla_fwd_workspace_bytes bytes,

@@ -72,9 +72,9 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
 // Auto dispatch: the single pass saves two kernel boundaries and one read of
 // k, v, gk, but every chunk reads O(sqrt(N)) published tiles. Measured on
 // MI355X (64/64, chunk 64) it is ahead for chains of up to 32 chunks on grids
-// of up to a few thousand chunk-heads, and behind beyond either.
+// of up to about a thousand chunk-heads, and behind beyond either.
 constexpr int kOnepassMaxChain = 32;
-constexpr long kOnepassMaxChunks = 3072;
+constexpr long kOnepassMaxChunks = 1024;
 
 bool single_pass_fits(const gla::Problem& p) {
   const int nb_max = p.B < gla::kMaxBatchPerLaunch ? p.B : gla::kMaxBatchPerLaunch;

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       if (u < DKDV / 8) {
         const int d = u / (DV / 8), e8 = (u % (DV / 8)) * 8;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sS[e8 + c][d] = h8[it][c];
+        for (int c = 0; c < 8; ++c) sS[e8 + c][swz<DK>(e8 + c, d)] = h8[it][c];
       }
     }
   }
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         qt[e] = qf[e] * fexp2(sc[e]);
         kt[e] = kf[e] * fexp2(tt[c] - sc[e]);
         k8[c] = (half_t)kt[e];
-        if constexpr (kFused) sKh[d][t] = (half_t)(kt[e] * ff[c]);
+        if constexpr (kFused) sKh[d][swz<C>(d, t)] = (half_t)(kt[e] * ff[c]);
       }
       *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = k8;
     }
@@ -214,8 +214,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         const int E = blk / ND, D = blk % ND;
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
-          const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
-          const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][16 * J + 4 * lq]);
+          const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
+          const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][swz<C>(16 * D + lr, 16 * J + 4 * lq)]);
           uacc[i] = mfma16x16x16(a, bb, uacc[i]);
         }
       }
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const half4 sb =
-                *reinterpret_cast<const half4*>(&sS[16 * E + lr][32 * ks + lk + 4 * hh]);
+                *reinterpret_cast<const half4*>(&sS[16 * E + lr][swz<DK>(16 * E + lr, 32 * ks + lk + 4 * hh)]);
             const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
                                 : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
             acc = mfma16x16x16(qa, sb, acc);
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
           if (J <= I) {
-            const half4 vb = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
+            const half4 vb = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
             acc = mfma16x16x16(A[J], vb, acc);
           }
         }
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
           if (J <= I) {
-            const half4 vb = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
+            const half4 vb = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
             oacc[E] = mfma16x16x16(A[J], vb, oacc[E]);
           }
         }
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
           store_f8(sfin + bh * DKDV + x8, f);
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sS[x8 % DV + c][d] = (half_t)xs[g][c];
+        for (int c = 0; c < 8; ++c) sS[x8 % DV + c][swz<DK>(x8 % DV + c, d)] = (half_t)xs[g][c];
       }
     }
     // -- every read of published data is done: count it; the last clears the chain
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const half4 sb =
-                *reinterpret_cast<const half4*>(&sS[16 * E + lr][32 * ks + lk + 4 * hh]);
+                *reinterpret_cast<const half4*>(&sS[16 * E + lr][swz<DK>(16 * E + lr, 32 * ks + lk + 4 * hh)]);
             const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
                                 : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
             oacc[E] = mfma16x16x16(qa, sb, oacc[E]);

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
       lds8(&sAft[I][32 * ks + lk], aft);
 #pragma unroll
       for (int c = 0; c < 8; ++c)  // B - b_t: the decay of the later tokens
-        sKh[32 * ks + lk + c][t] = (half_t)(kf[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
+        sKh[32 * ks + lk + c][swz<C>(32 * ks + lk + c, t)] =
+            (half_t)(kf[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
     }
   }
   __syncthreads();
@@ -117,8 +118,8 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
       const int E = blk / ND, D = blk % ND;
 #pragma unroll
       for (int J = 0; J < NB; ++J) {
-        const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][16 * J + 4 * lq]);
-        const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][16 * J + 4 * lq]);
+        const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
+        const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][swz<C>(16 * D + lr, 16 * J + 4 * lq)]);
         acc[i] = mfma16x16x16(a, bb, acc[i]);
       }
     }
@@ -299,6 +300,9 @@ WsLayout workspace_layout(const Problem& p) {
 }
 
 Segments onepass_segments(int N) {
+  // short chains: one segment (each chunk reads its <= 7 predecessors, one
+  // publication hop); longer ones: about sqrt(N) segments of sqrt(N) chunks
+  if (N <= 8) return Segments{N, 1};
   int G = 1;
   while (G * G < N) ++G;
   return Segments{G, (N + G - 1) / G};

@@ -24,7 +24,8 @@ struct WsLayout {
 
 WsLayout workspace_layout(const Problem& p);
 
-// Segments of the single-pass schedule: G chunks each (G = ceil(sqrt(N))).
+// Segments of the single-pass schedule: G chunks each (one segment of N
+// chunks up to N = 8, else G = ceil(sqrt(N))).
 struct Segments {
   int G, nseg;
 };

@@ -61,6 +61,17 @@ __device__ __forceinline__ void load_row(const InT* p, long row, int lk, float* 
     for (int c = 0; c < 8; ++c) x[8 * ks + c] = valid ? y[ks][c] : 0.f;
 }
 
+// Column swizzle of the half tiles that are written transposed (V^T, K^T,
+// S^T): column groups of 4 halves are permuted by row / 8, so that the eight
+// rows 8m + c that one 2-byte store instruction touches fall in different
+// LDS banks, while every 4-element run a matrix-core operand read takes stays
+// contiguous. NCOLS (the logical row length) is a power of two >= 16.
+template <int NCOLS>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int M = NCOLS / 4 - 1 < 7 ? NCOLS / 4 - 1 : 7;
+  return col ^ (((row >> 3) & M) << 2);
+}
+
 // V rows of the chunk, transposed into sVt[e][token] (half); loads
 // unconditional as in load_row.
 template <int DV, int C, int VSTR, typename InT>
@@ -82,7 +93,7 @@ __device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT,
     if (u < C * (DV / 8)) {
       const bool valid = sRow[r] >= 0;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) sVt[c8 + c][r] = valid ? v8[it][c] : (half_t)0.f;
+      for (int c = 0; c < 8; ++c) sVt[c8 + c][swz<C>(c8 + c, r)] = valid ? v8[it][c] : (half_t)0.f;
     }
   }
 }
