@@ -492,12 +492,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         for (int c = 0; c < 8; ++c) sS[x8 % DV + c][swz<DK>(x8 % DV + c, d)] = (half_t)xs[g][c];
       }
     }
-    // -- every read of published data is done: count it; the last clears the chain
-    __syncthreads();
-    if (tid == 0) sDone = atomicAdd(cw + N + nseg, 1u);
-    __syncthreads();
-    if (sDone == (unsigned)(N - 1))
-      for (int i = tid; i < N + nseg + 1; i += kThreads) cw[i] = 0u;
+    __syncthreads();  // S_n complete in LDS; every read of published data done
     // -- readout, on the same accumulation chains: O_I += Q^_I S_n
     if (owner) {
 #pragma unroll
@@ -547,6 +542,17 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       }
     }
     if (sRow[r] >= 0) store8(op + orow * DV + c8, x);
+  }
+  if constexpr (kFused) {
+    // -- this chunk is done reading what its chain published: count it; the
+    // last chunk of the chain to finish clears the chain's control words (off
+    // the critical path, after the outputs are on their way)
+    if (tid == 0) sDone = atomicAdd(ctrl + kCtrlHeader + bh * (long)(N + nseg + 1) + N + nseg, 1u);
+    __syncthreads();
+    if (sDone == (unsigned)(N - 1)) {
+      unsigned* cw = ctrl + kCtrlHeader + bh * (long)(N + nseg + 1);
+      for (int i = tid; i < N + nseg + 1; i += kThreads) cw[i] = 0u;
+    }
   }
 }
 

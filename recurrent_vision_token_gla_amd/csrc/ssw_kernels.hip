@@ -14,6 +14,8 @@
 // weights of its 8 channels in registers and produces kItems outputs of 8
 // channels (16-byte loads and stores; a token's 64 channels are one
 // contiguous 128-byte run).
+#include <type_traits>
+
 #include "gla_launch.h"
 
 namespace gla {
@@ -23,6 +25,8 @@ constexpr int kTH = 8, kTW = 16, kCF = 64;  // tile rows, tile columns, channels
 constexpr int kGroups = kCF / 8;            // 8-channel groups per tile
 constexpr int kItems = kTH * kTW * kGroups / kThreads;  // outputs per thread
 constexpr int kHalo = (kTH + 2) * (kTW + 2);
+
+typedef float float8_t __attribute__((ext_vector_type(8)));  // 8 channels of float
 
 __device__ __forceinline__ float silu(float a) {
   // a * sigmoid(a); exp2 on the transcendental unit, reciprocal of 1 + e^-a
@@ -45,21 +49,29 @@ __global__ __launch_bounds__(kThreads) void ssw_kernel(const InT* __restrict__ a
   const long bT = (long)blockIdx.z * gh * gw;
   const int ngroups = min(kGroups, (F - c0) / 8);  // F is a multiple of 8
 
-  // -- halo tile of u: (kTH+2) x (kTW+2) tokens x kCF channels, zero outside
-  for (int it = tid; it < kHalo * kGroups; it += kThreads) {
+  // -- halo tile of u: (kTH+2) x (kTW+2) tokens x kCF channels, zero outside.
+  // A fixed number of clamped, unconditional loads per thread, all issued
+  // before the first LDS store waits on one.
+  constexpr int kHaloIt = (kHalo * kGroups + kThreads - 1) / kThreads;
+  typedef typename std::conditional<sizeof(InT) == 2, half8, float8_t>::type Vec;
+  Vec hv[kHaloIt];
+#pragma unroll
+  for (int k = 0; k < kHaloIt; ++k) {
+    const int it = min(tid + kThreads * k, kHalo * kGroups - 1);
     const int p = it / kGroups, g = it % kGroups;
     const int y = ty0 - 1 + p / (kTW + 2), x = tx0 - 1 + p % (kTW + 2);
-    const bool in = y >= 0 && y < gh && x >= 0 && x < gw && g < ngroups;
-    // unconditional load (clamped to a valid token), zeroed if outside
     const long tok = bT + (long)min(max(y, 0), gh - 1) * gw + min(max(x, 0), gw - 1);
-    const int cg = c0 + 8 * min(g, ngroups - 1);
-    float v[8];
-    load8(up + tok * F + cg, v);
-    StT s8[8];
+    hv[k] = *reinterpret_cast<const Vec*>(up + tok * F + c0 + 8 * min(g, ngroups - 1));
+  }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s8[c] = (StT)(in ? v[c] : 0.f);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) sU[p][8 * g + c] = s8[c];
+  for (int k = 0; k < kHaloIt; ++k) {
+    const int it = tid + kThreads * k;
+    if (it < kHalo * kGroups) {
+      const int p = it / kGroups, g = it % kGroups;
+      const int y = ty0 - 1 + p / (kTW + 2), x = tx0 - 1 + p % (kTW + 2);
+      const bool in = y >= 0 && y < gh && x >= 0 && x < gw && g < ngroups;
+      *reinterpret_cast<Vec*>(&sU[p][8 * g]) = in ? hv[k] : Vec{};
+    }
   }
 
   // -- this thread's channel group and its weights
@@ -73,13 +85,13 @@ __global__ __launch_bounds__(kThreads) void ssw_kernel(const InT* __restrict__ a
     for (int k = 0; k < 9; ++k) w[c][k] = wp[(long)(cg + c) * 9 + k];
     bias[c] = bp ? bp[cg + c] : 0.f;
   }
-  // gate inputs of this thread's outputs, loaded before the barrier
-  float av[kItems][8];
+  // gate-branch inputs of this thread's outputs (clamped to valid tokens)
+  Vec avv[kItems];
 #pragma unroll
   for (int i = 0; i < kItems; ++i) {
     const int p = tid / kGroups + (kThreads / kGroups) * i;  // token within the tile
     const int y = min(ty0 + p / kTW, gh - 1), x = min(tx0 + p % kTW, gw - 1);
-    load8(ap + (bT + (long)y * gw + x) * F + cg, av[i]);
+    avv[i] = *reinterpret_cast<const Vec*>(ap + (bT + (long)y * gw + x) * F + cg);
   }
   __syncthreads();
 
@@ -88,6 +100,9 @@ __global__ __launch_bounds__(kThreads) void ssw_kernel(const InT* __restrict__ a
     const int p = tid / kGroups + (kThreads / kGroups) * i;
     const int ly = p / kTW, lx = p % kTW;
     const int y = ty0 + ly, x = tx0 + lx;
+    float av[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) av[c] = (float)avv[i][c];
     float acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = bias[c];
@@ -103,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void ssw_kernel(const InT* __restrict__ a
     if (gvalid && y < gh && x < gw) {
       float out[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) out[c] = silu(av[i][c]) * acc[c];
+      for (int c = 0; c < 8; ++c) out[c] = silu(av[c]) * acc[c];
       store8(hp + (bT + (long)y * gw + x) * F + cg, out);
     }
   }
