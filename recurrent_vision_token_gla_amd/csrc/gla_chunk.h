@@ -57,21 +57,23 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
   constexpr int NPAIR = NB * (NB - 1) / 2;
   constexpr int DKDV = DK * DV;
-  constexpr int KSTR = DK + 8;  // halves, rows of K~ and S^T
-  constexpr int VSTR = C + 8;   // halves, rows of V^T and K^T
-  constexpr int USTR = DV + 8;  // halves, rows of the U staging tile
-  constexpr int OSTR = DV + 8;  // rows of the output staging tile
+  constexpr int KSTR = DK + 8;   // halves, rows of K~ (read along key dims)
+  constexpr int VSTR = DV + 16;  // halves, rows of V (read transposed)
+  constexpr int HSTR = DK + 16;  // halves, rows of K^ (read transposed)
+  constexpr int SSTR = DV + 16;  // halves, rows of S (read transposed)
+  constexpr int USTR = DV + 8;   // halves, rows of the U staging tile
+  constexpr int OSTR = DV + 8;   // rows of the output staging tile
   constexpr int NGR = (DKDV / 8 + kThreads - 1) / kThreads;  // state groups of 8 per thread
   constexpr int LB = 4;  // predecessors per batch of look-back loads
   constexpr float kHalfRange = 8.f, kF32Range = 120.f;  // log2 decay per sub-block
   // K~ is dead once the score blocks are built; the output tile reuses it
   constexpr int KO_BYTES = (C * KSTR * 2 > C * OSTR * (int)sizeof(InT)) ? C * KSTR * 2
                                                                         : C * OSTR * (int)sizeof(InT);
-  // one region in turn holds K^T, the U staging tile and S^T (only S^T unfused)
-  constexpr int X0 = DV * KSTR * 2, X1 = kFused ? DK * VSTR * 2 : 0, X2 = kFused ? DK * USTR * 2 : 0;
+  // one region in turn holds K^, the U staging tile and S (only S unfused)
+  constexpr int X0 = DK * SSTR * 2, X1 = kFused ? C * HSTR * 2 : 0, X2 = kFused ? DK * USTR * 2 : 0;
   constexpr int X_BYTES = X0 > X1 ? (X0 > X2 ? X0 : X2) : (X1 > X2 ? X1 : X2);
   __shared__ __attribute__((aligned(16))) char sKO[KO_BYTES];
-  __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
+  __shared__ __attribute__((aligned(16))) half_t sV[C][VSTR];
   __shared__ __attribute__((aligned(16))) char sX[X_BYTES];
   __shared__ __attribute__((aligned(16))) float sTot[NB][DK], sS7[NB][DK];
   __shared__ __attribute__((aligned(16))) float sEb[NB][DK], sR1[NB][DK], sR2[NB][DK];
@@ -83,8 +85,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __shared__ unsigned sDone;
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
-  half_t (*sS)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sX);
-  half_t (*sKh)[VSTR] = reinterpret_cast<half_t (*)[VSTR]>(sX);
+  half_t (*sS)[SSTR] = reinterpret_cast<half_t (*)[SSTR]>(sX);
+  half_t (*sKh)[HSTR] = reinterpret_cast<half_t (*)[HSTR]>(sX);
   half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sX);
 
   int n, h, b;
@@ -114,9 +116,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     load_row<DK, NKS>(kp, row, lk, kf);
     load_row<DK, NKS>(gp, row, lk, sc);
   }
-  // -- the entering state (stored [dk][dv], staged transposed as sS[e][d];
-  // three-phase schedule only) and the chunk's V^T, through LDS; every load
-  // is issued before the first LDS write that waits on one
+  // -- the entering state (stored [dk][dv], staged as rows sS[d][e]; three-
+  // phase schedule only) and the chunk's V rows, through LDS; every load is
+  // issued before the first LDS write that waits on one
   constexpr int NSIT = kFused ? 1 : (DKDV / 8 + kThreads - 1) / kThreads;
   half8 h8[NSIT];
   if constexpr (!kFused) {
@@ -124,15 +126,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) h8[it] = load8h(Sb + 8 * ((tid + kThreads * it) % (DKDV / 8)));
   }
-  load_vt<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sVt);
+  load_v<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sV);
   if constexpr (!kFused) {
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) {
       const int u = tid + kThreads * it;
       if (u < DKDV / 8) {
         const int d = u / (DV / 8), e8 = (u % (DV / 8)) * 8;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sS[e8 + c][swz<DK>(e8 + c, d)] = h8[it][c];
+        *reinterpret_cast<half8*>(&sS[d][e8]) = h8[it];
       }
     }
   }
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   }
   __syncthreads();
   // -- per-element factors; K~ goes to LDS for the other sub-blocks, and in
-  // one pass K^ = K~ 2^(totals of the later sub-blocks), transposed, for U
+  // one pass K^ = K~ 2^(totals of the later sub-blocks), for U
   float qt[NEL], kt[NEL];
   if (owner) {
 #pragma unroll
@@ -186,16 +187,17 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       float tt[8], ff[8];
       lds8(&sTot[I][32 * ks + lk], tt);
       if constexpr (kFused) lds8(&sF[I][32 * ks + lk], ff);
-      half8 k8;
+      half8 k8, kh8;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const int e = 8 * ks + c, d = 32 * ks + lk + c;
+        const int e = 8 * ks + c;
         qt[e] = qf[e] * fexp2(sc[e]);
         kt[e] = kf[e] * fexp2(tt[c] - sc[e]);
         k8[c] = (half_t)kt[e];
-        if constexpr (kFused) sKh[d][swz<C>(d, t)] = (half_t)(kt[e] * ff[c]);
+        if constexpr (kFused) kh8[c] = (half_t)(kt[e] * ff[c]);
       }
       *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = k8;
+      if constexpr (kFused) *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = kh8;
     }
   }
   __syncthreads();
@@ -214,13 +216,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         const int E = blk / ND, D = blk % ND;
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
-          const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
-          const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][swz<C>(16 * D + lr, 16 * J + 4 * lq)]);
+          const half4 a = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
+          const half4 bb = ld_tr<HSTR, 4>(&sKh[16 * J][16 * D]);
           uacc[i] = mfma16x16x16(a, bb, uacc[i]);
         }
       }
     }
-    __syncthreads();  // K^T is no longer read: the region becomes the U staging tile
+    __syncthreads();  // K^ is no longer read: the region becomes the U staging tile
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int blk = wave + 4 * i;
@@ -339,8 +341,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const half4 sb =
-                *reinterpret_cast<const half4*>(&sS[16 * E + lr][swz<DK>(16 * E + lr, 32 * ks + lk + 4 * hh)]);
+            const half4 sb = ld_tr<SSTR, 8>(&sS[32 * ks + 4 * hh][16 * E]);
             const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
                                 : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
             acc = mfma16x16x16(qa, sb, acc);
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
           if (J <= I) {
-            const half4 vb = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
+            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
             acc = mfma16x16x16(A[J], vb, acc);
           }
         }
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
           if (J <= I) {
-            const half4 vb = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
+            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
             oacc[E] = mfma16x16x16(A[J], vb, oacc[E]);
           }
         }
@@ -488,8 +489,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
           for (int c = 0; c < 8; ++c) f[c] = sAn[d] * xs[g][c] + (float)un[c];
           store_f8(sfin + bh * DKDV + x8, f);
         }
+        half8 s8;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sS[x8 % DV + c][swz<DK>(x8 % DV + c, d)] = (half_t)xs[g][c];
+        for (int c = 0; c < 8; ++c) s8[c] = (half_t)xs[g][c];
+        *reinterpret_cast<half8*>(&sS[d][x8 % DV]) = s8;
       }
     }
     __syncthreads();  // S_n complete in LDS; every read of published data done
@@ -501,8 +504,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const half4 sb =
-                *reinterpret_cast<const half4*>(&sS[16 * E + lr][swz<DK>(16 * E + lr, 32 * ks + lk + 4 * hh)]);
+            const half4 sb = ld_tr<SSTR, 8>(&sS[32 * ks + 4 * hh][16 * E]);
             const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
                                 : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
             oacc[E] = mfma16x16x16(qa, sb, oacc[E]);

@@ -36,9 +36,9 @@ namespace tile {
 //   a[d]      = 2^(B[d])
 // Wave w owns the 16 tokens of sub-block w, one token per lane row, and
 // takes its cumulative decay with a DPP row scan plus the totals of the
-// earlier sub-blocks. K^ goes to LDS transposed (token-contiguous per key
-// dim), V likewise, so both operands of the token contraction are 8-byte
-// LDS reads; U is produced (as U^T) in 16x16 blocks on the matrix cores,
+// earlier sub-blocks. K^ and V go to LDS as token rows (16-byte stores) and
+// both operands of the token contraction come back through the transposing
+// LDS read; U is produced (as U^T) in 16x16 blocks on the matrix cores,
 // staged through LDS as rows of key dims and stored as half [dk][dv].
 // ===========================================================================
 template <int DK, int DV, int C, typename InT>
@@ -47,16 +47,17 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     half_t* __restrict__ Uws, float* __restrict__ Aws, int T, int H, int N, int gh, int gw,
     DirPack dirs) {
   constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
-  constexpr int VSTR = C + 8;    // halves, token-contiguous rows
+  constexpr int VSTR = DV + 16;  // halves, rows of V (read transposed)
+  constexpr int HSTR = DK + 16;  // halves, rows of K^ (read transposed)
   constexpr int USTR = DV + 8;   // halves, staging rows of U (one row per key dim)
-  // the U staging tile reuses K^T's LDS once the products have read it
-  constexpr int KU_BYTES = (VSTR > USTR ? VSTR : USTR) * DK * 2;
-  __shared__ __attribute__((aligned(16))) half_t sVt[DV][VSTR];
+  // the U staging tile reuses K^'s LDS once the products have read it
+  constexpr int KU_BYTES = (C * HSTR > DK * USTR ? C * HSTR : DK * USTR) * 2;
+  __shared__ __attribute__((aligned(16))) half_t sV[C][VSTR];
   __shared__ __attribute__((aligned(16))) char sKU[KU_BYTES];
   __shared__ __attribute__((aligned(16))) float sTot[NB][DK];
   __shared__ __attribute__((aligned(16))) float sAft[NB][DK];  // totals of sub-blocks I..NB-1
   __shared__ int sRow[C];
-  half_t (*sKh)[VSTR] = reinterpret_cast<half_t (*)[VSTR]>(sKU);
+  half_t (*sKh)[HSTR] = reinterpret_cast<half_t (*)[HSTR]>(sKU);
   half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sKU);
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     load_row<DK, NKS>(kp, row, lk, kf);
     load_row<DK, NKS>(gp, row, lk, sc);
   }
-  load_vt<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sVt);
+  load_v<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sV);
   if (owner) {
 #pragma unroll
     for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e] * kLog2e);
@@ -100,10 +101,11 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     for (int ks = 0; ks < NKS; ++ks) {
       float aft[8];
       lds8(&sAft[I][32 * ks + lk], aft);
+      half8 kh8;
 #pragma unroll
       for (int c = 0; c < 8; ++c)  // B - b_t: the decay of the later tokens
-        sKh[32 * ks + lk + c][swz<C>(32 * ks + lk + c, t)] =
-            (half_t)(kf[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
+        kh8[c] = (half_t)(kf[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
+      *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = kh8;
     }
   }
   __syncthreads();
@@ -118,13 +120,13 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
       const int E = blk / ND, D = blk % ND;
 #pragma unroll
       for (int J = 0; J < NB; ++J) {
-        const half4 a = *reinterpret_cast<const half4*>(&sVt[16 * E + lr][swz<C>(16 * E + lr, 16 * J + 4 * lq)]);
-        const half4 bb = *reinterpret_cast<const half4*>(&sKh[16 * D + lr][swz<C>(16 * D + lr, 16 * J + 4 * lq)]);
+        const half4 a = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
+        const half4 bb = ld_tr<HSTR, 4>(&sKh[16 * J][16 * D]);
         acc[i] = mfma16x16x16(a, bb, acc[i]);
       }
     }
   }
-  __syncthreads();  // K^T is no longer read
+  __syncthreads();  // K^ is no longer read
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int blk = wave + 4 * i;

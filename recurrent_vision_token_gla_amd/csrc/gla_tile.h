@@ -61,22 +61,31 @@ __device__ __forceinline__ void load_row(const InT* p, long row, int lk, float* 
     for (int c = 0; c < 8; ++c) x[8 * ks + c] = valid ? y[ks][c] : 0.f;
 }
 
-// Column swizzle of the half tiles that are written transposed (V^T, K^T,
-// S^T): column groups of 4 halves are permuted by row / 8, so that the eight
-// rows 8m + c that one 2-byte store instruction touches fall in different
-// LDS banks, while every 4-element run a matrix-core operand read takes stays
-// contiguous. NCOLS (the logical row length) is a power of two >= 16.
-template <int NCOLS>
-__device__ __forceinline__ int swz(int row, int col) {
-  constexpr int M = NCOLS / 4 - 1 < 7 ? NCOLS / 4 - 1 : 7;
-  return col ^ (((row >> 3) & M) << 2);
+// A 16x16 block of a row-major half tile in LDS, read through the LDS unit's
+// transposing read (ds_read_b64_tr_b16). blk = &tile[R0][c0]; lane
+// (i = lane % 16, q = lane / 16) receives rows R0 + GSTEP*q + 0..3 of column
+// c0 + i: the matrix-core operand layout of a block whose rows run along the
+// contraction (the B operand of the 16x16x16 product, or the A operand of the
+// transposed product). The read works within each group of 16 lanes: source
+// lane s supplies four consecutive halves (row GSTEP*q + s/4, columns
+// 4*(s%4)..+3) and lane i receives element i%4 of source lane 4k + i/4 as its
+// k-th value. Rows are 8-byte aligned (STR a multiple of 4); a row stride of
+// 16 halves modulo 64 keeps the four rows of a lane group in distinct banks.
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
+
+template <int STR, int GSTEP>
+__device__ __forceinline__ half4 ld_tr(const half_t* blk) {
+  const int s = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+  const half_t* p = blk + (GSTEP * q + (s >> 2)) * STR + 4 * (s & 3);
+  return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)p));
 }
 
-// V rows of the chunk, transposed into sVt[e][token] (half); loads
-// unconditional as in load_row.
+// V rows of the chunk into sV[token][e] (half, zero for padding rows) with
+// 16-byte stores; loads unconditional as in load_row.
 template <int DV, int C, int VSTR, typename InT>
-__device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT, int H, int h,
-                                        half_t (*sVt)[VSTR]) {
+__device__ __forceinline__ void load_v(const InT* vp, const int* sRow, long bT, int H, int h,
+                                       half_t (*sV)[VSTR]) {
   constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
   half8 v8[NIT];
 #pragma unroll
@@ -92,8 +101,10 @@ __device__ __forceinline__ void load_vt(const InT* vp, const int* sRow, long bT,
     const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
     if (u < C * (DV / 8)) {
       const bool valid = sRow[r] >= 0;
+      half8 x;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) sVt[c8 + c][swz<C>(c8 + c, r)] = valid ? v8[it][c] : (half_t)0.f;
+      for (int c = 0; c < 8; ++c) x[c] = valid ? v8[it][c] : (half_t)0.f;
+      *reinterpret_cast<half8*>(&sV[r][c8]) = x;
     }
   }
 }
