@@ -38,13 +38,15 @@ namespace tile {
 // chunk only ever waits on chunks of lower index, which were dispatched
 // earlier. Each chunk
 //   1. computes its summary U_n and decay a_n and publishes them;
-//   2. computes its intra-chunk part A V while its predecessors publish;
-//   3. takes the state it enters, in two levels over segments of G chunks:
+//   2. takes the state it enters, in two levels over segments of G chunks:
 //        S_n = X + W (.) P,  X = sum_{s0 <= m < n} (prod_{m<j<n} a_j) (.) U_m,
 //        W = prod_{s0 <= j < n} a_j,  P = state entering the segment
 //      where P composes the aggregates (prod a, sum of decayed U) that the
 //      last chunk of each earlier segment publishes (and the initial state);
-//   4. adds the readout Q^ S_n and stores the outputs.
+//      the in-segment part X, W comes first, so the segment's last chunk
+//      publishes its aggregate before it computes its intra-chunk part A V
+//      (the other chunks compute theirs while the aggregates arrive);
+//   3. adds the readout Q^ S_n and stores the outputs.
 // ===========================================================================
 template <int DK, int DV, int C, typename InT, bool kFused, bool kGate>
 __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __shared__ float sAn[kFused ? DK : 1];
   __shared__ int sRow[C];
   __shared__ int sTier;
-  __shared__ unsigned sDone;
+  __shared__ unsigned sDone, sPub;
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
   half_t (*sS)[SSTR] = reinterpret_cast<half_t (*)[SSTR]>(sX);
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
   chunk_rows<C>(sRow, n * C, T, gh, gw, dirs.get(b));
-  if (tid == 0) sTier = 0;
+  if (tid == 0) sTier = 0, sPub = 0u;
   __syncthreads();
 
   // -- this wave's token rows of q, k, gk in the operand layout (waves past
@@ -156,23 +158,32 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // -- per (sub-block, key dim) factors, one key dim per thread
   if (tid < NB * DK) {
     const int I2 = tid / DK, d = tid % DK;
-    float beta = 0.f;
-    for (int J = 0; J < I2; ++J) beta += sTot[J][d];
-    const float tot = sTot[I2][d], s7 = sS7[I2][d];
+    float tots[NB];  // every sub-block's total, read together
+#pragma unroll
+    for (int J = 0; J < NB; ++J) tots[J] = sTot[J][d];
+    const float s7 = sS7[I2][d];
+    float beta = 0.f, tot = 0.f, after = 0.f;  // totals before, of and after I2
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      if (J < I2) beta += tots[J];
+      else if (J == I2) tot = tots[J];
+      else after += tots[J];
+    }
     sEb[I2][d] = fexp2(beta);
     sR1[I2][d] = fexp2(-s7);
     sR2[I2][d] = fexp2(s7 - tot);
     float acc = 0.f;  // log2 of m_{I2,J} for J = I2-1, I2-2, ...
-    for (int J = I2 - 1; J >= 0; --J) {
-      sM[I2 * (I2 - 1) / 2 + J][d] = fexp2(acc);
-      acc += sTot[J][d];
+#pragma unroll
+    for (int J = NB - 2; J >= 0; --J) {
+      if (J < I2) {
+        sM[I2 * (I2 - 1) / 2 + J][d] = fexp2(acc);
+        acc += tots[J];
+      }
     }
     const float range = -tot;
     if (!(range <= kF32Range)) atomicMax(&sTier, 2);
     else if (!(range <= kHalfRange)) atomicMax(&sTier, 1);
     if constexpr (kFused) {
-      float after = 0.f;  // totals of the later sub-blocks
-      for (int J = I2 + 1; J < NB; ++J) after += sTot[J][d];
       sF[I2][d] = fexp2(after);
       if (I2 == NB - 1) sAn[d] = fexp2(beta + tot);  // a_n = 2^(chunk total)
     }
@@ -205,7 +216,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   unsigned* cw = nullptr;  // this chain's control words
   if constexpr (kFused) {
     cw = ctrl + kCtrlHeader + bh * (long)(N + nseg + 1);
-    // -- U_n^T = V^T K^ in 16x16 blocks, staged as rows of key dims, published
+    // -- U_n^T = V^T K^ in 16x16 blocks, staged as rows of key dims (the
+    // tile stays in LDS until the segment's aggregate is built), published
     constexpr int NBLK = NE * ND, BPW = (NBLK + 3) / 4;
     floatx4 uacc[BPW];
 #pragma unroll
@@ -359,23 +371,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       }
     }
   } else {
-    // -- intra-chunk part first: O_I = sum_{J<=I} A_IJ V_J
-    floatx4 oacc[NE];
-#pragma unroll
-    for (int E = 0; E < NE; ++E) {
-      oacc[E] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (owner) {
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J <= I) {
-            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
-            oacc[E] = mfma16x16x16(A[J], vb, oacc[E]);
-          }
-        }
-      }
-    }
     // -- the entering state, in-segment part: X and W
     const int seg = n / G, n0 = seg * G, nlast = min(n0 + G, N) - 1;
+    const bool agg = n == nlast && seg < nseg - 1;  // publishes the segment's aggregate
     if (wave == 0) wave_wait_flags(cw + n0, n - n0, ctrl);
     __syncthreads();
     float xs[NGR][8], wv[NGR];
@@ -409,18 +407,19 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             for (int c = 0; c < 8; ++c) xs[g][c] += wv[g] * (float)u[g][j][c];
             wv[g] *= a[g][j];
           }
+          consume(u[g][j], a[g][j]);
         }
       }
     }
     // -- the last chunk of a segment publishes the segment's aggregate
-    if (n == nlast && seg < nseg - 1) {
+    if (agg) {
       const long gs = bh * nseg + seg;
 #pragma unroll
       for (int g = 0; g < NGR; ++g) {
         const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
         if (x8 < DKDV) {
           half8 ag;
-          const half8 un = ld_dev(Uws + bhn * DKDV + x8);  // this chunk's own U_n
+          const half8 un = *reinterpret_cast<const half8*>(&sU[d][x8 % DV]);  // own U_n
 #pragma unroll
           for (int c = 0; c < 8; ++c) ag[c] = (half_t)(sAn[d] * xs[g][c] + (float)un[c]);
           st_dev(Sws + gs * DKDV + x8, ag);
@@ -432,8 +431,24 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
         if (x8 < DKDV && x8 % DV == 0) st_dev(GAws + gs * DK + d, wv[g] * sAn[d]);
       }
-      publish(cw + N + seg);
     }
+    // -- intra-chunk part, while the aggregate's stores complete and the
+    // earlier segments publish: O_I = sum_{J<=I} A_IJ V_J
+    floatx4 oacc[NE];
+#pragma unroll
+    for (int E = 0; E < NE; ++E) {
+      oacc[E] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (owner) {
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+          if (J <= I) {
+            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
+            oacc[E] = mfma16x16x16(A[J], vb, oacc[E]);
+          }
+        }
+      }
+    }
+    if (agg) publish_wave(cw + N + seg, &sPub);
     // -- the state entering the segment, from the earlier segments' aggregates
     if (wave == 0) wave_wait_flags(cw + N, seg, ctrl);
     __syncthreads();
@@ -467,6 +482,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             for (int c = 0; c < 8; ++c) pv[g][c] += w2[g] * (float)u[g][j][c];
             w2[g] *= a[g][j];
           }
+          consume(u[g][j], a[g][j]);
         }
       }
     }

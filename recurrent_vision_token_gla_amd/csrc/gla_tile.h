@@ -145,8 +145,8 @@ constexpr long kSpinLimit = 1L << 21;  // polls of one wait (seconds, far above 
 // atomic accesses (relaxed, 8 or 4 bytes). Those are coherent across the
 // XCDs' L2 caches by themselves, so publishing needs no L2 write-back and
 // reading no L2 invalidation, which would cost every workgroup on the XCD:
-//   publisher: coherent stores; each wave waits for their completion;
-//              barrier; one flag store.
+//   publisher: coherent stores; each wave waits for their completion and
+//              counts itself in LDS; the last one stores the flag.
 //   reader:    one wave polls the flags; barrier; coherent loads.
 typedef unsigned long u64x2 __attribute__((ext_vector_type(2)));
 
@@ -170,6 +170,15 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Marks loaded registers as read on every path. A load whose result a
+// branch skips stays outstanding past the join for the compiler's wait
+// insertion, so the next write of that register would wait for all memory
+// operations issued since (stores included); here the wait comes where the
+// value is consumed anyway.
+__device__ __forceinline__ void consume(const half8& u, const float& a) {
+  asm volatile("" ::"v"(u), "v"(a));
+}
+
 // Lane i of the calling wave watches flags[i], i < count <= 64. Returns once
 // every watched flag is set, or when the poll budget runs out (recorded in
 // *err). The caller then passes a workgroup barrier before reading.
@@ -189,12 +198,14 @@ __device__ __forceinline__ void wave_wait_flags(const unsigned* flags, int count
   }
 }
 
-// Every wave waits until its coherent stores have completed, then one flag
-// is set. Must be reached by the whole workgroup.
-__device__ __forceinline__ void publish(unsigned* flag) {
+// Called once by every wave of the workgroup after it has issued its
+// coherent stores of one publication: the wave waits for their completion
+// and counts itself in *count (LDS, zero beforehand); the last wave to arrive
+// sets the flag. No workgroup barrier, so a wave that arrives early goes on.
+__device__ __forceinline__ void publish_wave(unsigned* flag, unsigned* count) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((threadIdx.x & 63) == 0 && atomicAdd(count, 1u) == kThreads / 64 - 1)
+    __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace tile
