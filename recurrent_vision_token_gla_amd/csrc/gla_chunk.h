@@ -214,6 +214,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __syncthreads();
 
   unsigned* cw = nullptr;  // this chain's control words
+  // this chain's summaries and segment aggregates (single pass only)
+  const __amdgpu_buffer_rsrc_t rU = coh_rsrc(Uws + bh * N * DKDV, (long)N * DKDV);
+  const __amdgpu_buffer_rsrc_t rS = coh_rsrc(Sws + bh * nseg * DKDV, (long)nseg * DKDV);
   if constexpr (kFused) {
     cw = ctrl + kCtrlHeader + bh * (long)(N + nseg + 1);
     // -- U_n^T = V^T K^ in 16x16 blocks, staged as rows of key dims (the
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     // on to their score blocks without waiting for the stores to complete
     if (wave == 0) {
       for (int x8 = 8 * lane; x8 < DKDV; x8 += 8 * 64)
-        st_dev(Uws + bhn * DKDV + x8, *reinterpret_cast<const half8*>(&sU[x8 / DV][x8 % DV]));
+        st_coh(rU, n * DKDV + x8, *reinterpret_cast<const half8*>(&sU[x8 / DV][x8 % DV]));
       for (int d = lane; d < DK; d += 64) st_dev(Aws + bhn * DK + d, sAn[d]);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (lane == 0) __hip_atomic_store(cw + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -392,8 +395,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         const int x8 = (8 * (tid + kThreads * g)) % DKDV;
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
-          const long mj = m - j >= n0 ? m - j : n0;
-          u[g][j] = ld_dev(Uws + (bh * N + mj) * DKDV + x8);
+          const int mj = m - j >= n0 ? m - j : n0;
+          u[g][j] = ld_coh(rU, mj * DKDV + x8);
           a[g][j] = ld_dev(Aws + (bh * N + mj) * DK + x8 / DV);
         }
       }
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
           const half8 un = *reinterpret_cast<const half8*>(&sU[d][x8 % DV]);  // own U_n
 #pragma unroll
           for (int c = 0; c < 8; ++c) ag[c] = (half_t)(sAn[d] * xs[g][c] + (float)un[c]);
-          st_dev(Sws + gs * DKDV + x8, ag);
+          st_coh(rS, seg * DKDV + x8, ag);
         }
       }
       // the segment's decay: the weight the look-back accumulated, times a_n
@@ -467,8 +470,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         const int x8 = (8 * (tid + kThreads * g)) % DKDV;
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
-          const long sj = s2 - j >= 0 ? s2 - j : 0;
-          u[g][j] = ld_dev(Sws + (bh * nseg + sj) * DKDV + x8);
+          const int sj = s2 - j >= 0 ? s2 - j : 0;
+          u[g][j] = ld_coh(rS, sj * DKDV + x8);
           a[g][j] = ld_dev(GAws + (bh * nseg + sj) * DK + x8 / DV);
         }
       }
@@ -486,6 +489,18 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         }
       }
     }
+    // the chain's last chunk also returns the state after it, a_n S_n + U_n:
+    // its own U_n comes from the staging tile, read before S overwrites it
+    const bool fin = sfin != nullptr && n == N - 1;
+    half8 ul[NGR];
+    if (fin) {
+#pragma unroll
+      for (int g = 0; g < NGR; ++g) {
+        const int x8 = (8 * (tid + kThreads * g)) % DKDV;
+        ul[g] = *reinterpret_cast<const half8*>(&sU[x8 / DV][x8 % DV]);
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int g = 0; g < NGR; ++g) {
       const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
@@ -498,11 +513,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) xs[g][c] += wv[g] * pv[g][c];  // S_n
-        if (sfin && n == N - 1) {
+        if (fin) {
           float f[8];
-          const half8 un = ld_dev(Uws + bhn * DKDV + x8);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) f[c] = sAn[d] * xs[g][c] + (float)un[c];
+          for (int c = 0; c < 8; ++c) f[c] = sAn[d] * xs[g][c] + (float)ul[g][c];
           store_f8(sfin + bh * DKDV + x8, f);
         }
         half8 s8;

@@ -148,21 +148,25 @@ constexpr long kSpinLimit = 1L << 21;  // polls of one wait (seconds, far above 
 //   publisher: coherent stores; each wave waits for their completion and
 //              counts itself in LDS; the last one stores the flag.
 //   reader:    one wave polls the flags; barrier; coherent loads.
-typedef unsigned long u64x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void st_dev(half_t* p, half8 v) {
-  const u64x2 w = __builtin_bit_cast(u64x2, v);
-  unsigned long* q = reinterpret_cast<unsigned long*>(p);
-  __hip_atomic_store(q, w.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, w.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Tiles of half (U, segment aggregates) move as 16-byte buffer accesses with
+// the device-scope cache policy (sc1): the coherence of the atomics below,
+// one instruction per 16 bytes (two interleaved 8-byte atomics would write
+// every 32-byte sector twice). The resource covers one chain's array;
+// accesses outside it read zero and write nothing.
+constexpr int kCohDevice = 16;  // cache-policy bits: sc1
+constexpr unsigned kBufWord3 = 0x00020000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const half_t* base, long halves) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(base), 0, (int)(2 * halves), kBufWord3);
 }
-__device__ __forceinline__ half8 ld_dev(const half_t* p) {
-  const unsigned long* q = reinterpret_cast<const unsigned long*>(p);
-  u64x2 w;
-  w.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  w.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_bit_cast(half8, w);
+__device__ __forceinline__ void st_coh(__amdgpu_buffer_rsrc_t r, int half_off, half8 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, 2 * half_off, 0, kCohDevice);
 }
+__device__ __forceinline__ half8 ld_coh(__amdgpu_buffer_rsrc_t r, int half_off) {
+  return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, 2 * half_off, 0, kCohDevice));
+}
+
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
