@@ -47,8 +47,9 @@
  * segments, whose last chunks publish segment aggregates), and adds the
  * readout. Workgroups run in chain-major order and only wait on earlier
  * ones, with bounded waits. gla_fwd picks the single pass for chains of at
- * most 32 chunks on grids of at most 1024 chunk-heads (if the launch fits
- * its control words), and the three phases otherwise.
+ * most 32 chunks, and for chains of at most 64 chunks on grids of at most 512
+ * chunk-heads (in both cases if the launch fits its control words), and the
+ * three phases otherwise.
  *
  * Workspace: caller-owned device memory of gla_fwd_workspace_bytes bytes,
  * 256-byte aligned. Its first 64 KiB are control words of the single pass;

@@ -71,10 +71,13 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
 
 // Auto dispatch: the single pass saves two kernel boundaries and one read of
 // k, v, gk, but every chunk reads O(sqrt(N)) published tiles. Measured on
-// MI355X (64/64, chunk 64) it is ahead for chains of up to 32 chunks on grids
-// of up to about a thousand chunk-heads, and behind beyond either.
-constexpr int kOnepassMaxChain = 32;
-constexpr long kOnepassMaxChunks = 1024;
+// MI355X (64/64, chunk 64) it is ahead at every grid size tried for chains of
+// up to 25 chunks (to 12,288 chunk-heads), ahead at a few hundred chunk-heads
+// for chains of 49 and 64 chunks and behind at 1,500 and more, and behind
+// for chains of 100 chunks and longer.
+constexpr int kOnepassAnyGrid = 32;      // chains this short: single pass at any grid
+constexpr int kOnepassMaxChain = 64;     // up to here: on small grids only
+constexpr long kOnepassMaxChunks = 512;  // chunk-heads of such a small grid
 
 bool single_pass_fits(const gla::Problem& p) {
   const int nb_max = p.B < gla::kMaxBatchPerLaunch ? p.B : gla::kMaxBatchPerLaunch;
@@ -82,7 +85,8 @@ bool single_pass_fits(const gla::Problem& p) {
 }
 
 bool prefer_single_pass(const gla::Problem& p) {
-  return p.N <= kOnepassMaxChain && (long)p.B * p.H * p.N <= kOnepassMaxChunks;
+  return p.N <= kOnepassAnyGrid ||
+         (p.N <= kOnepassMaxChain && (long)p.B * p.H * p.N <= kOnepassMaxChunks);
 }
 
 int outputs_impl(const void* q, const void* k, const void* v, const void* gk, void* o, int B,
