@@ -102,9 +102,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
-  chunk_rows<C>(sRow, n * C, T, gh, gw, dirs.get(b));
+  const int dir = dirs.get(b);
+  // the row table (for the scatter) and the flags below are first read after
+  // the barrier that follows the cumulative sums
+  chunk_rows<C>(sRow, n * C, T, gh, gw, dir);
   if (tid == 0) sTier = 0, sPub = 0u;
-  __syncthreads();
 
   // -- this wave's token rows of q, k, gk in the operand layout (waves past
   // the last sub-block load a padding row too: no branch around the loads)
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   const int I = wave, t = 16 * I + lr;
   float qf[NEL], kf[NEL], sc[NEL];
   {
-    const int rr = owner ? sRow[t] : -1;
+    const int rr = owner ? token_row(n * C + t, T, gh, gw, dir) : -1;
     const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
     load_row<DK, NKS>(qp, row, lk, qf);
     load_row<DK, NKS>(kp, row, lk, kf);
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) h8[it] = load8h(Sb + 8 * ((tid + kThreads * it) % (DKDV / 8)));
   }
-  load_v<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sV);
+  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV);
   if constexpr (!kFused) {
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) {

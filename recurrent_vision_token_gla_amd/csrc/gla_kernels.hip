@@ -56,7 +56,6 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
   __shared__ __attribute__((aligned(16))) char sKU[KU_BYTES];
   __shared__ __attribute__((aligned(16))) float sTot[NB][DK];
   __shared__ __attribute__((aligned(16))) float sAft[NB][DK];  // totals of sub-blocks I..NB-1
-  __shared__ int sRow[C];
   half_t (*sKh)[HSTR] = reinterpret_cast<half_t (*)[HSTR]>(sKU);
   half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sKU);
 
@@ -64,19 +63,18 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
-  chunk_rows<C>(sRow, n * C, T, gh, gw, dirs.get(b));
-  __syncthreads();
+  const int dir = dirs.get(b);
 
   const bool owner = wave < NB;
   const int I = wave, t = 16 * I + lr;
   float kf[NEL], sc[NEL];
   {
-    const int rr = owner ? sRow[t] : -1;
+    const int rr = owner ? token_row(n * C + t, T, gh, gw, dir) : -1;
     const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
     load_row<DK, NKS>(kp, row, lk, kf);
     load_row<DK, NKS>(gp, row, lk, sc);
   }
-  load_v<DV, C, VSTR>(vp, sRow, (long)b * T, H, h, sV);
+  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV);
   if (owner) {
 #pragma unroll
     for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e] * kLog2e);

@@ -35,12 +35,15 @@ __device__ __forceinline__ floatx4 mfma16x16x16(half4 a, half4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// Raster row of every token of the chunk (-1 past the end of the sequence).
+// Raster row of scan position tok (-1 past the end of the sequence).
+__device__ __forceinline__ int token_row(int tok, int T, int gh, int gw, int dir) {
+  return tok < T ? scan_to_raster(tok, T, gh, gw, dir) : -1;
+}
+
+// Raster row of every token of the chunk, for the output scatter.
 template <int C>
 __device__ __forceinline__ void chunk_rows(int* sRow, int tok0, int T, int gh, int gw, int dir) {
-  const int tid = threadIdx.x;
-  const int L = min(C, T - tok0);
-  if (tid < C) sRow[tid] = tid < L ? scan_to_raster(tok0 + tid, T, gh, gw, dir) : -1;
+  if (threadIdx.x < C) sRow[threadIdx.x] = token_row(tok0 + threadIdx.x, T, gh, gw, dir);
 }
 
 // Token row t of a [B][T][H][D] tensor, this lane's 8*NKS dims
@@ -81,26 +84,29 @@ __device__ __forceinline__ half4 ld_tr(const half_t* blk) {
   return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)p));
 }
 
-// V rows of the chunk into sV[token][e] (half, zero for padding rows) with
-// 16-byte stores; loads unconditional as in load_row.
+// V rows of the chunk (scan positions tok0..tok0+C-1) into sV[token][e]
+// (half, zero for padding rows) with 16-byte stores; each thread finds its
+// rows' raster positions itself, and the loads are unconditional as in
+// load_row.
 template <int DV, int C, int VSTR, typename InT>
-__device__ __forceinline__ void load_v(const InT* vp, const int* sRow, long bT, int H, int h,
-                                       half_t (*sV)[VSTR]) {
+__device__ __forceinline__ void load_v(const InT* vp, int tok0, int T, int gh, int gw, int dir,
+                                       long bT, int H, int h, half_t (*sV)[VSTR]) {
   constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
   half8 v8[NIT];
+  int rows[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int u = threadIdx.x + kThreads * it;
     const int r = (u / (DV / 8)) % C, c8 = (u % (DV / 8)) * 8;
-    const int row = sRow[r] >= 0 ? sRow[r] : 0;
-    v8[it] = load8h(vp + ((bT + row) * H + h) * DV + c8);
+    rows[it] = token_row(tok0 + r, T, gh, gw, dir);
+    v8[it] = load8h(vp + ((bT + (rows[it] >= 0 ? rows[it] : 0)) * H + h) * DV + c8);
   }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int u = threadIdx.x + kThreads * it;
     const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
     if (u < C * (DV / 8)) {
-      const bool valid = sRow[r] >= 0;
+      const bool valid = rows[it] >= 0;
       half8 x;
 #pragma unroll
       for (int c = 0; c < 8; ++c) x[c] = valid ? v8[it][c] : (half_t)0.f;
