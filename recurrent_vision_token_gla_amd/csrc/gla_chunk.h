@@ -113,9 +113,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   const bool owner = wave < NB;
   const int I = wave, t = 16 * I + lr;
   float qf[NEL], kf[NEL], sc[NEL];
+  bool pad;  // this lane's token row is padding
   {
     const int rr = owner ? token_row(n * C + t, T, gh, gw, dir) : -1;
     const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
+    pad = row < 0;
     load_row<DK, NKS>(qp, row, lk, qf);
     load_row<DK, NKS>(kp, row, lk, kf);
     load_row<DK, NKS>(gp, row, lk, sc);
@@ -142,6 +144,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     }
   }
 
+  if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
+    zero_row<NEL>(pad, qf);
+    zero_row<NEL>(pad, kf);
+    zero_row<NEL>(pad, sc);
+  }
   // -- in-sub-block inclusive cumsum along tokens (DPP row scan)
   if (owner) {
 #pragma unroll
@@ -556,6 +563,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   for (int u = tid; u < C * LPR; u += kThreads) {
     const int r = u / LPR, c8 = (u % LPR) * 8;
     const long orow = ((long)b * T + (sRow[r] >= 0 ? sRow[r] : 0)) * H + h;
+    if constexpr (!kGate) {
+      if (sRow[r] >= 0) copy8(op + orow * DV + c8, &sO[r][c8]);
+      continue;
+    }
     float x[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[c] = (float)sO[r][c8 + c];

@@ -34,9 +34,23 @@ struct DirPack {
 // Works": four scan orders over the patch grid). Left->right is raster
 // order; top->bottom walks columns left to right, each top to bottom;
 // right->left and bottom->top reverse those two sequences.
+// The column walk's t / gh and t % gh: below 2^22 tokens through a float
+// reciprocal (the quotient t/gh < 2^22, so the rounded product is within
+// 0.75 of it and one step corrects the truncation), else integer division.
 __device__ __forceinline__ int scan_to_raster(int t, int T, int gh, int gw, int dir) {
-  if (dir & 1) t = T - 1 - t;               // R2L (1) and B2T (3) reverse
-  if (dir & 2) return (t % gh) * gw + t / gh;  // T2B (2) and B2T (3)
+  if (dir & 1) t = T - 1 - t;  // R2L (1) and B2T (3) reverse
+  if (dir & 2) {               // T2B (2) and B2T (3)
+    int q, r;
+    if (T < (1 << 22)) {
+      q = (int)((float)t * __builtin_amdgcn_rcpf((float)gh));
+      r = t - q * gh;
+      if (r < 0) --q, r += gh;
+      else if (r >= gh) ++q, r -= gh;
+    } else {
+      q = t / gh, r = t % gh;
+    }
+    return r * gw + q;
+  }
   return t;
 }
 
@@ -70,6 +84,14 @@ __device__ __forceinline__ void store8(half_t* p, const float (&x)[8]) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) h[c] = (half_t)x[c];
   *reinterpret_cast<half8*>(p) = h;
+}
+// Eight consecutive elements copied as they are (16 or 32 bytes).
+__device__ __forceinline__ void copy8(half_t* dst, const half_t* src) {
+  *reinterpret_cast<half8*>(dst) = *reinterpret_cast<const half8*>(src);
+}
+__device__ __forceinline__ void copy8(float* dst, const float* src) {
+  *reinterpret_cast<floatx4*>(dst) = *reinterpret_cast<const floatx4*>(src);
+  *reinterpret_cast<floatx4*>(dst + 4) = *reinterpret_cast<const floatx4*>(src + 4);
 }
 __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
   floatx4 a = {x[0], x[1], x[2], x[3]};

@@ -68,13 +68,19 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
   const bool owner = wave < NB;
   const int I = wave, t = 16 * I + lr;
   float kf[NEL], sc[NEL];
+  bool pad;  // this lane's token row is padding
   {
     const int rr = owner ? token_row(n * C + t, T, gh, gw, dir) : -1;
     const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
+    pad = row < 0;
     load_row<DK, NKS>(kp, row, lk, kf);
     load_row<DK, NKS>(gp, row, lk, sc);
   }
   load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV);
+  if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
+    zero_row<NEL>(pad, kf);
+    zero_row<NEL>(pad, sc);
+  }
   if (owner) {
 #pragma unroll
     for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e] * kLog2e);

@@ -51,17 +51,24 @@ __device__ __forceinline__ void chunk_rows(int* sRow, int tok0, int T, int gh, i
 // unconditional (a padding row reads row 0 and is zeroed afterwards): a load
 // under a divergent branch would be waited for before the branches rejoin,
 // which would serialize every load of the kernel's prologue.
+// A padding row's values are zeroed by zero_row afterwards, once every
+// prologue load is in flight, and only in a chain's last chunk (a branch
+// right after the loads would wait for them).
 template <int D, int NKS, typename InT>
 __device__ __forceinline__ void load_row(const InT* p, long row, int lk, float* x) {
-  const bool valid = row >= 0;
-  const InT* r = p + (valid ? row : 0) * D + lk;
+  const InT* r = p + (row >= 0 ? row : 0) * D + lk;
   float y[NKS][8];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) load8(r + 32 * ks, y[ks]);
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) x[8 * ks + c] = valid ? y[ks][c] : 0.f;
+    for (int c = 0; c < 8; ++c) x[8 * ks + c] = y[ks][c];
+}
+template <int NEL>
+__device__ __forceinline__ void zero_row(bool pad, float* x) {
+#pragma unroll
+  for (int e = 0; e < NEL; ++e) x[e] = pad ? 0.f : x[e];
 }
 
 // A 16x16 block of a row-major half tile in LDS, read through the LDS unit's
@@ -106,10 +113,8 @@ __device__ __forceinline__ void load_v(const InT* vp, int tok0, int T, int gh, i
     const int u = threadIdx.x + kThreads * it;
     const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
     if (u < C * (DV / 8)) {
-      const bool valid = rows[it] >= 0;
-      half8 x;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) x[c] = valid ? v8[it][c] : (half_t)0.f;
+      half8 x = v8[it];
+      if (tok0 + C > T && rows[it] < 0) x = half8{};  // padding row (last chunk only)
       *reinterpret_cast<half8*>(&sV[r][c8]) = x;
     }
   }
