@@ -24,8 +24,12 @@ def _device():
 
 
 # ---------------------------------------------------------------- scan order
+# the large grids exercise the column walk's float-reciprocal division near its
+# 2^22-token limit (prime heights, the largest quotients) and the integer
+# division beyond it
 @pytest.mark.parametrize("grid", [(1, 1), (1, 7), (7, 1), (5, 7), (8, 8), (13, 3), (40, 40),
-                                  (80, 80), (128, 128), (3, 200)])
+                                  (80, 80), (128, 128), (3, 200), (1021, 4093), (3, 1398101),
+                                  (2048, 2048), (2049, 2047)])
 def test_scan_perm_bit_exact(grid):
     gh, gw = grid
     for d in range(4):
