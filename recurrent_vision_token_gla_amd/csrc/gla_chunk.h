@@ -65,12 +65,20 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   constexpr int SSTR = DV + 16;  // halves, rows of S (read transposed)
   constexpr int USTR = DV + 8;   // halves, rows of the U staging tile
   constexpr int OSTR = DV + 8;   // rows of the output staging tile
+  // the single pass's plain half output is staged column-major (rows = value
+  // columns, 8-byte stores from the accumulators) and read back as token rows
+  // through the transposing LDS read: fewer LDS operations on its critical
+  // path. Each store then covers half a token row, which costs the
+  // throughput-bound three-phase kernel more than it saves; it, the gated
+  // and the fp32 outputs keep token rows.
+  constexpr bool kColO = kFused && !kGate && sizeof(InT) == 2;
+  constexpr int OTSTR = C + 16;  // halves, rows of the column-major output tile
   constexpr int NGR = (DKDV / 8 + kThreads - 1) / kThreads;  // state groups of 8 per thread
   constexpr int LB = 4;  // predecessors per batch of look-back loads
   constexpr float kHalfRange = 8.f, kF32Range = 120.f;  // log2 decay per sub-block
   // K~ is dead once the score blocks are built; the output tile reuses it
-  constexpr int KO_BYTES = (C * KSTR * 2 > C * OSTR * (int)sizeof(InT)) ? C * KSTR * 2
-                                                                        : C * OSTR * (int)sizeof(InT);
+  constexpr int KO0 = C * KSTR * 2, KO1 = kColO ? DV * OTSTR * 2 : C * OSTR * (int)sizeof(InT);
+  constexpr int KO_BYTES = KO0 > KO1 ? KO0 : KO1;
   // one region in turn holds K^, the U staging tile and S (only S unfused)
   constexpr int X0 = DK * SSTR * 2, X1 = kFused ? C * HSTR * 2 : 0, X2 = kFused ? DK * USTR * 2 : 0;
   constexpr int X_BYTES = X0 > X1 ? (X0 > X2 ? X0 : X2) : (X1 > X2 ? X1 : X2);
@@ -87,6 +95,21 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __shared__ unsigned sDone, sPub;
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
+  half_t (*sOT)[OTSTR] = reinterpret_cast<half_t (*)[OTSTR]>(sKO);
+  // output block (sub-block I, value block E) of this lane: rows 16I + 4lq + r,
+  // column 16E + lr
+  auto stage_out = [&](const floatx4& acc, int E) {
+    const int I = threadIdx.x >> 6, lq = (threadIdx.x >> 4) & 3, lr = threadIdx.x & 15;
+    if constexpr (kColO) {
+      half4 hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = (half_t)acc[r];
+      *reinterpret_cast<half4*>(&sOT[16 * E + lr][16 * I + 4 * lq]) = hv;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (InT)acc[r];
+    }
+  };
   half_t (*sS)[SSTR] = reinterpret_cast<half_t (*)[SSTR]>(sX);
   half_t (*sKh)[HSTR] = reinterpret_cast<half_t (*)[HSTR]>(sX);
   half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sX);
@@ -378,8 +401,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             acc = mfma16x16x16(A[J], vb, acc);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (InT)acc[r];
+        stage_out(acc, E);
       }
     }
   } else {
@@ -549,8 +571,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             oacc[E] = mfma16x16x16(qa, sb, oacc[E]);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (InT)oacc[E][r];
+        stage_out(oacc[E], E);
       }
     }
   }
@@ -560,7 +581,20 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // each row of dv values becomes o / sqrt(mean(o^2) + eps) * w * silu(z)
   // (its dv/8 lanes are neighbours and reduce the sum of squares by shuffles)
   constexpr int LPR = DV / 8;  // lanes per output row
-  for (int u = tid; u < C * LPR; u += kThreads) {
+  if constexpr (kColO) {
+    // unit (token block tb, value half eh): lane (lr, lq) takes token
+    // 16tb + lr, values 32eh + 8lq + 0..7, in two transposing reads
+    constexpr int NTB = C / 16, NU = NTB * (DV / 32);
+    for (int u = wave; u < NU; u += kThreads / 64) {
+      const int tb = u % NTB, eh = u / NTB, t = 16 * tb + lr;
+      const half4 lo = ld_tr<OTSTR, 8>(&sOT[32 * eh][16 * tb]);
+      const half4 hi = ld_tr<OTSTR, 8>(&sOT[32 * eh + 4][16 * tb]);
+      if (sRow[t] >= 0)
+        *reinterpret_cast<half8*>(op + (((long)b * T + sRow[t]) * H + h) * DV + 32 * eh + 8 * lq) =
+            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+  for (int u = tid; u < (kColO ? 0 : C * LPR); u += kThreads) {
     const int r = u / LPR, c8 = (u % LPR) * 8;
     const long orow = ((long)b * T + (sRow[r] >= 0 ? sRow[r] : 0)) * H + h;
     if constexpr (!kGate) {
