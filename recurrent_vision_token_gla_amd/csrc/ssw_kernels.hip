@@ -124,11 +124,217 @@ __global__ __launch_bounds__(kThreads) void ssw_kernel(const InT* __restrict__ a
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent, double-buffered form. A grid of about three workgroups per CU
+// walks the (batch, channel block, tile) units with a stride. While a unit
+// is computed from one LDS buffer, the next unit's halo tile streams into the
+// other with buffer loads that write LDS directly (lane l of a load lands 16 *
+// l bytes past the wave's base; a position outside the grid or the channels
+// gets an offset past its buffer's end and reads zero, which is the zero
+// padding), and its gate inputs into registers. The 3x3 weights and biases
+// (fp32) also come by direct loads, into one LDS buffer that is refilled once
+// every thread has copied the current unit's into registers. Each unit then
+// costs about the longer of its loads and its arithmetic, and no round of
+// workgroups runs partly empty.
+// ---------------------------------------------------------------------------
+template <typename InT>
+struct SswPipe {
+  static constexpr int kUPT = kCF * (int)sizeof(InT) / 16;  // 16-byte units per halo token
+  static constexpr int kUnits = kHalo * kUPT;               // of the halo tile
+  static constexpr int kFull = kUnits / kThreads;           // rounds every wave loads
+  static constexpr int kRemWaves = (kUnits - kFull * kThreads + 63) / 64;  // waves of the last round
+  static constexpr int kHaloBytes = (kFull * kThreads + kRemWaves * 64) * 16;
+  static constexpr int kWBytes = 3 * 64 * 16;  // 576 fp32 weights: 144 units, three waves' loads
+  static constexpr int kBBytes = 64 * 16;      // 64 fp32 biases: 16 units, one wave's load
+  static constexpr int kLdsBytes = 2 * kHaloBytes + kWBytes + kBBytes;
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename InT>
+__global__ __launch_bounds__(kThreads, 3) void ssw_persistent(
+    const InT* __restrict__ ap, const InT* __restrict__ up, const float* __restrict__ wp,
+    const float* __restrict__ bp, InT* __restrict__ hp, int gh, int gw, int F, int tiles_w,
+    int ntiles, int ncb, int nunits) {
+  using P = SswPipe<InT>;
+  using StT = InT;
+  typedef typename std::conditional<sizeof(InT) == 2, half8, float8_t>::type Vec;
+  __shared__ __attribute__((aligned(16))) char smem[P::kLdsBytes];
+  char* sW = smem + 2 * P::kHaloBytes;  // weights [64][9], then biases [64]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = tid % kGroups;
+  const long T = (long)gh * gw;
+  const int wnum = F * 9 * 4, bnum = bp ? F * 4 : 0;  // bytes of weights and biases
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wp), 0, wnum, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(bp), 0, bnum, 0x00020000);
+
+  struct Unit {
+    int b, cb, ty0, tx0;
+  };
+  // units numbered channel block fastest: the workgroups running at one time
+  // cover whole token rows of the [T][F] tensors
+  auto unit = [&](int id) {
+    const int cb = id % ncb, r = id / ncb, tile = r % ntiles;
+    return Unit{r / ntiles, cb, (tile / tiles_w) * kTH, (tile % tiles_w) * kTW};
+  };
+  // halo tile of unit U into buffer buf: every wave issues kFull loads, the
+  // first kRemWaves one more
+  auto load_halo = [&](const Unit& U, int buf) {
+    const unsigned nbytes = (unsigned)(T * F * (long)sizeof(InT));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<InT*>(up + (long)U.b * T * F), 0, (int)nbytes, 0x00020000);
+    char* base = smem + buf * P::kHaloBytes + 1024 * wave;
+    const int c0 = U.cb * kCF;
+#pragma unroll
+    for (int k = 0; k <= P::kFull; ++k) {
+      if (k == P::kFull && wave >= P::kRemWaves) break;
+      const int it = tid + kThreads * k;
+      const int p = it / P::kUPT, e = (it % P::kUPT) * (16 / (int)sizeof(StT));  // token, channel
+      const int y = U.ty0 - 1 + p / (kTW + 2), x = U.tx0 - 1 + p % (kTW + 2);
+      const bool in = it < P::kUnits && y >= 0 && y < gh && x >= 0 && x < gw && c0 + e < F;
+      const unsigned off = in ? (unsigned)((((long)y * gw + x) * F + c0 + e) * sizeof(InT)) : nbytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(base + kThreads * 16 * k), 16, off, 0, 0, 0);
+    }
+  };
+  // weights and biases of channel block cb: waves 0-2 load the 144 weight
+  // units, wave 3 the 16 bias units (one load per wave)
+  auto load_wb = [&](int cb) {
+    const int j = 64 * wave + lane;
+    if (wave < 3) {
+      const unsigned off = j < 144 ? (unsigned)(cb * kCF * 9 * 4 + 16 * j) : (unsigned)wnum;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(sW + 1024 * wave), 16, off, 0, 0, 0);
+    } else {
+      const unsigned off = lane < 16 ? (unsigned)(cb * kCF * 4 + 16 * lane) : (unsigned)bnum;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(sW + P::kWBytes), 16, off, 0, 0, 0);
+    }
+  };
+  // gate-branch input of output i of this thread (clamped to a valid token)
+  auto load_a = [&](const Unit& U, int i) {
+    const int cg = min(U.cb * kCF + 8 * g, F - 8);
+    const int p = tid / kGroups + (kThreads / kGroups) * i;
+    const int y = min(U.ty0 + p / kTW, gh - 1), x = min(U.tx0 + p % kTW, gw - 1);
+    return *reinterpret_cast<const Vec*>(ap + ((long)U.b * T + (long)y * gw + x) * F + cg);
+  };
+
+  int id = blockIdx.x;
+  if (id >= nunits) return;
+  Unit cur = unit(id);
+  Vec av[kItems];  // gate inputs of the unit being computed; refilled item by item for the next
+  load_halo(cur, 0);
+  load_wb(cur.cb);
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) av[i] = load_a(cur, i);
+  for (int k = 0;; ++k) {
+    const int nid = id + gridDim.x;
+    const bool more = nid < nunits;
+    const Unit nxt = unit(more ? nid : id);
+    if (more) {
+      load_halo(nxt, (k + 1) & 1);
+      // everything issued before the next unit's halo (this unit's halo,
+      // weights, biases and gate inputs, the previous unit's stores) is
+      // complete once no more than that halo's loads are outstanding
+      if (wave < P::kRemWaves) wait_vm<P::kFull + 1>();
+      else wait_vm<P::kFull>();
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();
+    // -- this thread's channel group: weights and biases into registers
+    const int c0 = cur.cb * kCF;
+    const bool gvalid = c0 + 8 * g < F;
+    float w[8][9], bias[8];
+    {
+      const float* sw = reinterpret_cast<const float*>(sW) + (8 * g) * 9;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int q = 0; q < 9; ++q) w[c][q] = sw[9 * c + q];
+      const float* sb = reinterpret_cast<const float*>(sW + P::kWBytes) + 8 * g;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) bias[c] = sb[c];
+    }
+    __syncthreads();  // every thread has its weights: the buffer takes the next unit's
+    if (more) load_wb(nxt.cb);
+    // -- outputs
+    const StT(*sU)[kCF] = reinterpret_cast<const StT(*)[kCF]>(smem + (k & 1) * P::kHaloBytes);
+    const long bT = (long)cur.b * T;
+    const int cg = c0 + 8 * g;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int p = tid / kGroups + (kThreads / kGroups) * i;
+      const int ly = p / kTW, lx = p % kTW;
+      const int y = cur.ty0 + ly, x = cur.tx0 + lx;
+      float acc[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = bias[c];
+#pragma unroll
+      for (int di = 0; di < 3; ++di) {
+#pragma unroll
+        for (int dj = 0; dj < 3; ++dj) {
+          const StT* sv = &sU[(ly + di) * (kTW + 2) + lx + dj][8 * g];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[c] += w[c][3 * di + dj] * (float)sv[c];
+        }
+      }
+      if (gvalid && y < gh && x < gw) {
+        float out[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) out[c] = silu((float)av[i][c]) * acc[c];
+        store8(hp + (bT + (long)y * gw + x) * F + cg, out);
+      }
+      if (more) av[i] = load_a(nxt, i);
+    }
+    if (!more) break;
+    __syncthreads();  // this buffer is free for the unit after next
+    id = nid;
+    cur = nxt;
+  }
+}
+
+template <typename InT>
+int ssw_blocks_per_cu() {
+  static int cached[64];  // per device; 0 = not yet known
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  if (cached[dev] == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ssw_persistent<InT>, kThreads, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    cached[dev] = nb;
+  }
+  return cached[dev];
+}
+
 template <typename InT>
 hipError_t ssw_t(const void* a, const void* u, const float* w, const float* bias, void* h, int B,
                  int gh, int gw, int F, hipStream_t s) {
   const int tiles_w = (gw + kTW - 1) / kTW, tiles_h = (gh + kTH - 1) / kTH;
-  dim3 grid(tiles_w * tiles_h, (F + kCF - 1) / kCF, B);
+  const int ncb = (F + kCF - 1) / kCF;
+  // the persistent form while one batch element's value tensor stays below
+  // 2^31 bytes (32-bit buffer offsets, plus the out-of-range offset)
+  if ((long)gh * gw * F * (long)sizeof(InT) < (1L << 31) && (long)F * 9 * 4 < (1L << 31)) {
+    const long nunits = (long)B * ncb * tiles_w * tiles_h;
+    if (nunits < (1L << 31)) {
+      int dev = 0, ncu = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+        ncu = 1;
+      const long cap = (long)ncu * ssw_blocks_per_cu<InT>();
+      const int grid = (int)(nunits < cap ? nunits : cap);
+      hipLaunchKernelGGL((ssw_persistent<InT>), dim3(grid), dim3(kThreads), 0, s,
+                         static_cast<const InT*>(a), static_cast<const InT*>(u), w, bias,
+                         static_cast<InT*>(h), gh, gw, F, tiles_w, tiles_w * tiles_h, ncb,
+                         (int)nunits);
+      return hipGetLastError();
+    }
+  }
+  dim3 grid(tiles_w * tiles_h, ncb, B);
   hipLaunchKernelGGL((ssw_kernel<InT>), grid, dim3(kThreads), 0, s, static_cast<const InT*>(a),
                      static_cast<const InT*>(u), w, bias, static_cast<InT*>(h), gh, gw, F,
                      tiles_w);
