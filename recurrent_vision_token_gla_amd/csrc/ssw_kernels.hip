@@ -13,7 +13,10 @@
 // tile with its one-token halo goes to LDS once; every thread keeps the 3x3
 // weights of its 8 channels in registers and produces kItems outputs of 8
 // channels (16-byte loads and stores; a token's 64 channels are one
-// contiguous 128-byte run).
+// contiguous 128-byte run). The persistent form further down is used whenever
+// ten grid rows of the value tensor fit a 32-bit buffer offset; the
+// grid-per-tile kernel that comes first covers wider grids.
+#include <cstdint>
 #include <type_traits>
 
 #include "gla_launch.h"
@@ -182,10 +185,15 @@ __global__ __launch_bounds__(kThreads, 3) void ssw_persistent(
   };
   // halo tile of unit U into buffer buf: every wave issues kFull loads, the
   // first kRemWaves one more
+  // the resource starts at the unit's first halo row (y = ty0 - 1, which may
+  // lie before the tensor: only positions inside the grid are read) and spans
+  // kTH + 2 grid rows, so offsets stay 32-bit for any number of rows
+  const unsigned nbytes = (unsigned)((long)(kTH + 2) * gw * F * (long)sizeof(InT));
   auto load_halo = [&](const Unit& U, int buf) {
-    const unsigned nbytes = (unsigned)(T * F * (long)sizeof(InT));
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<InT*>(up + (long)U.b * T * F), 0, (int)nbytes, 0x00020000);
+    const uintptr_t rbase = reinterpret_cast<uintptr_t>(up) +
+                            (uintptr_t)(((long)U.b * T + (long)(U.ty0 - 1) * gw) * F * (long)sizeof(InT));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(rbase), 0, (int)nbytes, 0x00020000);
     char* base = smem + buf * P::kHaloBytes + 1024 * wave;
     const int c0 = U.cb * kCF;
 #pragma unroll
@@ -193,9 +201,9 @@ __global__ __launch_bounds__(kThreads, 3) void ssw_persistent(
       if (k == P::kFull && wave >= P::kRemWaves) break;
       const int it = tid + kThreads * k;
       const int p = it / P::kUPT, e = (it % P::kUPT) * (16 / (int)sizeof(StT));  // token, channel
-      const int y = U.ty0 - 1 + p / (kTW + 2), x = U.tx0 - 1 + p % (kTW + 2);
+      const int py = p / (kTW + 2), y = U.ty0 - 1 + py, x = U.tx0 - 1 + p % (kTW + 2);
       const bool in = it < P::kUnits && y >= 0 && y < gh && x >= 0 && x < gw && c0 + e < F;
-      const unsigned off = in ? (unsigned)((((long)y * gw + x) * F + c0 + e) * sizeof(InT)) : nbytes;
+      const unsigned off = in ? (unsigned)((((long)py * gw + x) * F + c0 + e) * sizeof(InT)) : nbytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void*)(base + kThreads * 16 * k), 16, off, 0, 0, 0);
     }
@@ -316,9 +324,9 @@ hipError_t ssw_t(const void* a, const void* u, const float* w, const float* bias
                  int gh, int gw, int F, hipStream_t s) {
   const int tiles_w = (gw + kTW - 1) / kTW, tiles_h = (gh + kTH - 1) / kTH;
   const int ncb = (F + kCF - 1) / kCF;
-  // the persistent form while one batch element's value tensor stays below
+  // the persistent form while kTH + 2 grid rows of the value tensor stay below
   // 2^31 bytes (32-bit buffer offsets, plus the out-of-range offset)
-  if ((long)gh * gw * F * (long)sizeof(InT) < (1L << 31) && (long)F * 9 * 4 < (1L << 31)) {
+  if ((long)(kTH + 2) * gw * F * (long)sizeof(InT) < (1L << 31) && (long)F * 9 * 4 < (1L << 31)) {
     const long nunits = (long)B * ncb * tiles_w * tiles_h;
     if (nunits < (1L << 31)) {
       int dev = 0, ncu = 0;

@@ -73,3 +73,24 @@ def test_spatial_swiglu_argument_errors():
     b = torch.zeros((1, 16, 16), dtype=torch.float16, device="cuda")
     with pytest.raises(gla.GLAError):  # output aliases an input
         gla.spatial_swiglu(b, b.clone(), torch.zeros((16, 3, 3), device="cuda"), None, 4, 4, out=b)
+
+
+def test_spatial_swiglu_wide_grid_grid_per_tile_kernel():
+    """A grid so wide that ten rows of the value tensor pass 2^31 bytes takes
+    the grid-per-tile kernel (the persistent one addresses a unit's halo
+    rows with 32-bit offsets). Checked on column windows: the oracle runs on
+    each window plus its neighbour columns, and the window's tokens, whose
+    3x3 neighbourhoods lie inside, are compared."""
+    gh, gw, F = 1, 1 << 17, 1024
+    assert 10 * gw * F * 2 >= 1 << 31
+    a, u, w, bias = W.make_ssw_inputs(1, gh * gw, F, np.float16, seed=530)
+    h = _run(a, u, w, bias, gh, gw)
+    worst = 0.0
+    for x0 in (0, 5000, gw // 2 + 3, gw - 40):
+        lo, hi = max(0, x0 - 1), min(gw, x0 + 40 + 1)
+        ref = oracle.spatial_swiglu(a[:, lo:hi], u[:, lo:hi], w, bias, gh, hi - lo)
+        s = slice(x0 - lo, x0 - lo + 40)
+        err = rel_err(h[:, x0:x0 + 40], ref[:, s])
+        say(f"ssw wide grid window x0={x0}: rel_err={err:.3e}")
+        worst = max(worst, err)
+    assert worst <= TOL
