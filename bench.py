@@ -8,9 +8,12 @@ and the fraction of the HBM roofline reached.
 
 A step is one pass of the workload: one gla_fwd call per scan direction on
 that call's own seeded inputs, already resident in device memory. Steps are
-replayed from a captured HIP graph and timed with events on the launching
+replayed from captured HIP graphs and timed with events on the launching
 stream, mirroring the pages' protocol of event timing under graph replay
-(GTR project page, "Accuracy-Latency Frontier"). One JSON line is printed.
+(GTR project page, "Accuracy-Latency Frontier"). The headline rotates
+through copies of the step's inputs and outputs that together exceed twice
+the 256 MB Infinity Cache, so the bytes come from HBM; the same steps on one
+set of buffers (cache-warm) are reported beside it. One JSON line is printed.
 
   python bench.py [--steps K] [--warmup W] [--workload I] [--all]
 """
@@ -30,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "chunkwise GLA fwd tokens/s (fp16) at 1600/6400 tokens; % of roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+ROTATE_BYTES = 512 << 20  # rotating buffers: twice the 256 MB Infinity Cache
+MAX_SETS = 64
 KERNEL_SOURCES = ["gla_kernels.hip", "gla_chunk.h", "gla_tile.h", "gla_gated.hip",
                   "ssw_kernels.hip", "gla_device.h", "gla_launch.h"]
 
@@ -87,6 +92,38 @@ def load_traffic(kernel: str, workload: str):
     return None
 
 
+def _graph(torch, stream, fn):
+    """fn(s) captured once in a graph on a side stream (after one eager run)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            fn(s)
+    stream.wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_steps(torch, runs, steps, warmup):
+    """Milliseconds per step over exactly `steps` steps (runs replayed in
+    rotation), bracketed by synchronisations and timed with events."""
+    for i in range(warmup):
+        runs[i % len(runs)]()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        runs[i % len(runs)]()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, time.perf_counter() - wall0
+
+
 def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
     dev = torch.device("cuda:0")
     calls = []
@@ -95,93 +132,71 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
         tq, tk, tv, tg = (torch.from_numpy(x).to(dev) for x in (q, k, v, g))
         calls.append(dict(q=tq, k=tk, v=tv, g=tg, dirs=w.directions(c),
                           out=torch.empty_like(tv), host=(q, k, v, g)))
+    # rotating copies of every call's inputs and output (the contents do not
+    # matter to the caches; set 0 holds the originals)
+    step_bytes = sum(sum(c[n].numel() * c[n].element_size() for n in ("q", "k", "v", "g", "out"))
+                     for c in calls)
+    nsets = max(1, min(MAX_SETS, math.ceil(ROTATE_BYTES / step_bytes)))
+    sets = [calls] + [[dict(c, q=c["q"].clone(), k=c["k"].clone(), v=c["v"].clone(),
+                            g=c["g"].clone(), out=torch.empty_like(c["out"])) for c in calls]
+                      for _ in range(nsets - 1)]
     ws = gla.alloc_workspace(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, dev)
     stream = torch.cuda.current_stream()
 
-    def step(s=None):
-        for c in calls:
+    def step(cs, s=None):
+        for c in cs:
             gla.fwd(c["q"], c["k"], c["v"], c["g"], w.grid_h, w.grid_w, c["dirs"], w.chunk,
                     out=c["out"], workspace=ws, stream=s)
 
-    step()
+    for cs in sets:
+        step(cs)
     torch.cuda.synchronize()
-    graph = None
     if use_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(graph, stream=s):
-                step(s)
-        stream.wait_stream(s)
-        torch.cuda.synchronize()
-    run = graph.replay if graph is not None else step
+        graphs = [_graph(torch, stream, lambda s, cs=cs: step(cs, s)) for cs in sets]
+        runs = [g.replay for g in graphs]
+    else:
+        runs = [lambda cs=cs: step(cs) for cs in sets]
 
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(steps):
-        run()
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
-    ms_per_step = ms_total / steps
+    # headline: the sets in rotation; then the first set alone (cache-warm)
+    ms_per_step, wall = _time_steps(torch, runs, steps, warmup)
+    warm_ms, _ = _time_steps(torch, runs[:1], steps, warmup)
 
-    # median single-step latency (event pair per step)
+    # median single-step latency (event pair per step), rotating
     lat = []
-    for _ in range(min(50, max(10, steps // 4))):
+    for i in range(min(50, max(10, steps // 4))):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        run()
+        runs[i % nsets]()
         b.record()
         b.synchronize()
         lat.append(a.elapsed_time(b) * 1e3)
 
     # per-kernel durations: each kernel alone, `timing_reps` launches captured
-    # back to back in one graph (no host gaps), timed with events on the
-    # stream the kernels are launched on. The step's own schedule is the one
-    # gla_fwd picks; the other schedule's kernels are timed for reference.
-    c0 = calls[0]
+    # back to back in one graph (no host gaps) on the rotating sets, timed
+    # with events on the stream the kernels are launched on; and the same on
+    # the first set alone. The step's own schedule is the one gla_fwd picks;
+    # the other schedule's kernels are timed for reference.
     sched = gla.auto_schedule(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk)
 
-    def phases(s):
-        return {
-            "single_pass": lambda: gla.fwd(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
-                                           c0["dirs"], w.chunk, out=c0["out"], workspace=ws,
-                                           stream=s, schedule=gla.SCHED_SINGLE_PASS),
-            "summaries": lambda: gla.chunk_summaries(c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
-                                                     c0["dirs"], w.chunk, workspace=ws, stream=s),
-            "scan": lambda: gla.state_scan(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, ws,
-                                           stream=s),
-            "outputs": lambda: gla.chunk_outputs(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h,
-                                                 w.grid_w, c0["dirs"], w.chunk, workspace=ws,
-                                                 out=c0["out"], stream=s),
-        }
-
-    phase_us = {}
-    for name in ("single_pass", "summaries", "scan", "outputs"):
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        fn = phases(s)[name]
+    def phase(name, c0, s):
         if name == "single_pass":
-            try:
-                fn()  # rejected on the host (nothing launched) if it does not fit
-            except gla.GLAError:
-                continue
-        pg = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            fn()
-            with torch.cuda.graph(pg, stream=s):
-                for _ in range(timing_reps):
-                    fn()
-        stream.wait_stream(s)
-        torch.cuda.synchronize()
+            return gla.fwd(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w, c0["dirs"],
+                           w.chunk, out=c0["out"], workspace=ws, stream=s,
+                           schedule=gla.SCHED_SINGLE_PASS)
+        if name == "summaries":
+            return gla.chunk_summaries(c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w, c0["dirs"],
+                                       w.chunk, workspace=ws, stream=s)
+        if name == "scan":
+            return gla.state_scan(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk, ws, stream=s)
+        return gla.chunk_outputs(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w,
+                                 c0["dirs"], w.chunk, workspace=ws, out=c0["out"], stream=s)
+
+    def time_phase(name, rot):
+        def fn(s):
+            for r in range(timing_reps):
+                phase(name, sets[r % nsets][0] if rot else calls[0], s)
+        pg = _graph(torch, stream, fn)
         pg.replay()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
@@ -191,14 +206,32 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
             pg.replay()
         b.record()
         b.synchronize()
-        phase_us[name] = a.elapsed_time(b) * 1e3 / (3 * timing_reps)
-    # the full step ran last on the workspace: re-run it so outputs are current
-    run()
+        return a.elapsed_time(b) * 1e3 / (3 * timing_reps)
+
+    phase_us, phase_warm_us = {}, {}
+    for name in ("single_pass", "summaries", "scan", "outputs"):
+        if name == "single_pass":
+            try:
+                phase(name, calls[0], None)  # rejected on the host (nothing launched) if it does not fit
+            except gla.GLAError:
+                continue
+        phase_us[name] = time_phase(name, True)
+        phase_warm_us[name] = time_phase(name, False)
+    # the kernels ran last on the workspace: re-run the step so outputs are current
+    step(calls)
     torch.cuda.synchronize()
     used = ["single_pass"] if sched == gla.SCHED_SINGLE_PASS else ["summaries", "scan", "outputs"]
-    return dict(calls=calls, ms_per_step=ms_per_step, wall_s=wall, lat_us=lat,
-                phase_us=phase_us, ws=ws, used=used,
+    return dict(calls=calls, ms_per_step=ms_per_step, warm_ms_per_step=warm_ms, wall_s=wall,
+                lat_us=lat, phase_us=phase_us, phase_warm_us=phase_warm_us, ws=ws, used=used,
+                sets=nsets, set_bytes=step_bytes,
                 schedule="single_pass" if sched == gla.SCHED_SINGLE_PASS else "three_phase")
+
+
+def launch_floor_us(torch):
+    """Per-launch time of a one-element kernel, 20 captured back to back in one
+    graph: the floor any single kernel launch pays in this timing protocol."""
+    x = torch.zeros(1, device="cuda")
+    return time_graph(torch, lambda s: x.add_(1.0))
 
 
 def time_graph(torch, fn, reps=20, rounds=5):
@@ -300,8 +333,9 @@ def parity_check(w, res, oracle, np, max_bh=4):
     return max(errs)
 
 
-def cpu_baseline(w, res, oracle, target_s=3.0):
-    """The oracle, as it stands, timed on the host cores on the same inputs."""
+def cpu_baseline(w, res, oracle, target_s=10.0):
+    """The oracle, as it stands, timed on the host cores on the same inputs:
+    whole steps until about target_s seconds have passed."""
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -310,7 +344,7 @@ def cpu_baseline(w, res, oracle, target_s=3.0):
             oracle.gla_forward(q, k, v, g, w.grid_h, w.grid_w, c["dirs"])
         reps += 1
         el = time.perf_counter() - t0
-        if el >= target_s or reps >= 20:
+        if el >= target_s or reps >= 1000:
             break
     tokens = reps * w.calls * w.B * w.T
     return {"value": tokens / el, "unit": "tokens/s", "cores": oracle.oracle_threads(),
@@ -345,6 +379,11 @@ def summarize(w, res):
                      "avg_launch_us": res["phase_us"][dom]},
         "phase_us": res["phase_us"],
         "schedule": res["schedule"],
+        "warm": {"value": tokens_step / (res["warm_ms_per_step"] * 1e-3),
+                 "ms_per_step": res["warm_ms_per_step"],
+                 "call_us": res["warm_ms_per_step"] * 1e3 / w.calls,
+                 "kernel_us": res["phase_warm_us"]},
+        "rotation": {"sets": res["sets"], "bytes_per_set": res["set_bytes"]},
     }
 
 
@@ -394,9 +433,13 @@ def main():
           file=sys.stderr, flush=True)
     res = run_workload(w, args.steps, args.warmup, not args.no_graph, torch, gla, W)
     s = summarize(w, res)
-    print(f"# {w.name}: {s['value']:.4g} tokens/s, {s['call_us']:.2f} us/call, "
+    print(f"# {w.name}: {s['value']:.4g} tokens/s, {s['call_us']:.2f} us/call "
+          f"({s['rotation']['sets']} rotating sets; warm {s['warm']['call_us']:.2f}), "
           f"path {100 * s['path_roofline']['frac']:.1f}% of HBM roofline, {s['schedule']}; kernels "
           + ", ".join(f"{k} {v:.2f} us" for k, v in s["phase_us"].items()),
+          file=sys.stderr, flush=True)
+    floor = launch_floor_us(torch)
+    print(f"# launch floor (one-element kernel, graph-captured): {floor:.2f} us",
           file=sys.stderr, flush=True)
 
     import oracle
@@ -417,7 +460,8 @@ def main():
         ri = run_workload(wi, max(10, args.steps // 4), max(3, args.warmup // 4),
                           not args.no_graph, torch, gla, W)
         si = summarize(wi, ri)
-        print(f"# {wi.name}: {si['value']:.4g} tokens/s, {si['call_us']:.2f} us/call, path "
+        print(f"# {wi.name}: {si['value']:.4g} tokens/s, {si['call_us']:.2f} us/call "
+              f"({si['rotation']['sets']} rotating sets; warm {si['warm']['call_us']:.2f}), path "
               f"{100 * si['path_roofline']['frac']:.1f}% of HBM roofline, {si['schedule']}; kernels "
               + ", ".join(f"{k} {v:.2f} us" for k, v in si["phase_us"].items()),
               file=sys.stderr, flush=True)
@@ -425,7 +469,8 @@ def main():
                      "value": si["value"], "unit": "tokens/s", "us_per_call": si["call_us"],
                      "path_roofline_frac": si["path_roofline"]["frac"],
                      "schedule": si["schedule"], "dominant": si["dominant"],
-                     "dominant_frac": si["roofline"]["frac"], "kernel_us": si["phase_us"]})
+                     "dominant_frac": si["roofline"]["frac"], "kernel_us": si["phase_us"],
+                     "warm": si["warm"], "rotation": si["rotation"]})
         del ri
         torch.cuda.empty_cache()
 
@@ -463,6 +508,9 @@ def main():
         "median_step_latency_us": s["median_step_latency_us"],
         "schedule": s["schedule"],
         "kernel_us": s["phase_us"],
+        "warm": s["warm"],
+        "rotation": s["rotation"],
+        "launch_floor_us": floor,
         "parity_max_rel_err": parity,
         "cpu_baseline": cpu,
         "also": also,
