@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "chunkwise GLA fwd tokens/s (fp16) at 1600/6400 tokens; % of roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores, published
 ROTATE_BYTES = 512 << 20  # rotating buffers: twice the 256 MB Infinity Cache
 MAX_SETS = 64
 KERNEL_SOURCES = ["gla_kernels.hip", "gla_chunk.h", "gla_tile.h", "gla_gated.hip",
@@ -73,6 +74,18 @@ def phase_bytes(w):
         "scan": ch * (2 * w.dk * w.dv + 4 * w.dk + 2 * w.dk * w.dv),
         "outputs": th * (3 * w.dk + 2 * w.dv) * e + ch * 2 * w.dk * w.dv,
     }
+
+
+def phase_flops(w):
+    """Algorithmic matrix flops each kernel performs per launch (per
+    token-head: the summary K^T V and the readout Q S, 2 dk dv each; the
+    causal halves of the chunk's Q K^T and A V, C (dk + dv); the scan's
+    2 dk dv / C is negligible and not counted)."""
+    th = w.B * w.T * w.H
+    summ = 2 * w.dk * w.dv
+    outs = 2 * w.dk * w.dv + w.chunk * (w.dk + w.dv)
+    return {"single_pass": th * (summ + outs), "summaries": th * summ, "scan": 0,
+            "outputs": th * outs}
 
 
 def load_traffic(kernel: str, workload: str):
@@ -363,6 +376,9 @@ def summarize(w, res):
     used = {k: res["phase_us"][k] for k in res["used"]}
     dom = max(used, key=used.get)
     ach = pb[dom] / (res["phase_us"][dom] * 1e-6) / 1e9
+    fl = phase_flops(w)
+    tflops = fl[dom] / (res["phase_us"][dom] * 1e-6) / 1e12
+    path_flops = fl["single_pass"]
     return {
         "value": value,
         "call_us": call_us,
@@ -377,6 +393,10 @@ def summarize(w, res):
                      "traffic": load_traffic(dom, w.name),
                      "kernel": dom, "algorithmic_bytes_per_launch": pb[dom],
                      "avg_launch_us": res["phase_us"][dom]},
+        "mfma_roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+                          "kernel": dom, "algorithmic_flops_per_launch": fl[dom],
+                          "path_frac": path_flops / (call_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS},
         "phase_us": res["phase_us"],
         "schedule": res["schedule"],
         "warm": {"value": tokens_step / (res["warm_ms_per_step"] * 1e-3),
@@ -505,6 +525,7 @@ def main():
                    "timing": "eager" if args.no_graph else "graph_replay"},
         "roofline": s["roofline"],
         "path_roofline": s["path_roofline"],
+        "mfma_roofline": s["mfma_roofline"],
         "median_step_latency_us": s["median_step_latency_us"],
         "schedule": s["schedule"],
         "kernel_us": s["phase_us"],
