@@ -145,3 +145,20 @@ def test_single_pass_deterministic():
     a, _ = _run(x, gh, gw, [3], 64, gla.SCHED_SINGLE_PASS)
     b, _ = _run(x, gh, gw, [3], 64, gla.SCHED_SINGLE_PASS)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("sched", sorted(SCHEDS))
+def test_longest_single_pass_chain(sched):
+    """4,096 chunks in one chain (256 x 256 grid, chunk 16): the single pass's
+    widest waits (64 segments of 64 chunks) and the scan's longest segments
+    (256 chunks each, re-read past the register block), with a carried
+    state."""
+    gh, gw, chunk, B, H, dk, dv = 256, 256, 16, 1, 1, 32, 32
+    x = W.make_inputs(B, gh * gw, H, dk, dv, np.float16, seed=470)
+    s0 = np.random.default_rng(7).standard_normal((B, H, dk, dv)).astype(np.float32)
+    say(f"{sched} grid={gh}x{gw} chunk={chunk} N={gh * gw // chunk}")
+    o, sT = _run(x, gh, gw, [3], chunk, SCHEDS[sched], s0=s0)
+    ro, rs = oracle.gla_forward(*x, gh, gw, [3], s0=s0, return_state=True)
+    eo, es = rel_err(o, ro), rel_err(sT, rs)
+    say(f"  o err {eo:.2e}  S_T err {es:.2e}")
+    assert eo <= TOL and es <= TOL
