@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // -- in-sub-block inclusive cumsum along tokens (DPP row scan)
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e] * kLog2e);
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]) * kLog2e;
     if (lr == 15 || lr == 7) {
 #pragma unroll
       for (int e = 0; e < NEL; ++e) {

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
   }
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e] * kLog2e);
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]) * kLog2e;
     if (lr == 15) {
 #pragma unroll
       for (int e = 0; e < NEL; ++e) sTot[I][32 * (e / 8) + lk + (e % 8)] = sc[e];
