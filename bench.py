@@ -301,8 +301,9 @@ def token_sweep(torch, gla, W, np):
 
 
 def extra_kernels(torch, gla, W, np):
-    """The fused output gate at the 640^2 shape and the Spatial SwiGLU core on
-    its two workloads, each with its own HBM roofline fraction."""
+    """The fused output gate and the carried-state forward at the 640^2 shape
+    and the Spatial SwiGLU core on its two workloads, each with its own HBM
+    roofline fraction."""
     res = {}
     wl = W.WORKLOADS[1]
     q, k, v, gk = W.workload_inputs(wl, 0)
@@ -316,6 +317,17 @@ def extra_kernels(torch, gla, W, np):
                                                    stream=s))
     nbytes = wl.T * wl.H * (3 * wl.dk + 3 * wl.dv) * 2  # + the gate rows
     res["gated_" + wl.name] = {"us_per_call": us, "tokens_per_s": wl.T / (us * 1e-6),
+                               "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    # carried state: S_0 in, S_T out (fp32 [B][H][dk][dv] each) beside the forward
+    s0 = torch.from_numpy(np.random.default_rng(7300).standard_normal(
+        (wl.B, wl.H, wl.dk, wl.dv)).astype(np.float32)).cuda()
+    sT = torch.empty_like(s0)
+    o = torch.empty_like(tv)
+    us = time_graph(torch, lambda s: gla.fwd_state(tq, tk, tv, tg, wl.grid_h, wl.grid_w, [0],
+                                                   wl.chunk, s0=s0, s_final=sT, out=o,
+                                                   workspace=ws, stream=s))
+    nbytes = wl.T * wl.H * per_unit_bytes(wl) + 2 * wl.B * wl.H * wl.dk * wl.dv * 4
+    res["state_" + wl.name] = {"us_per_call": us, "tokens_per_s": wl.T / (us * 1e-6),
                                "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
     for sw in W.SSW_WORKLOADS:
         a, u, w, bias = W.make_ssw_inputs(sw.B, sw.T, sw.F, np.float16, seed=7200)
