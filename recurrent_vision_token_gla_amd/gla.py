@@ -145,8 +145,10 @@ def auto_schedule(B, H, grid_h, grid_w, dk, dv, chunk=64) -> int:
 
 def workspace_init(workspace: torch.Tensor, stream=None) -> None:
     """Zero the control words (and the sticky error word) with a kernel."""
-    _check(load().gla_workspace_init(workspace.data_ptr(), workspace.numel(),
-                                     _stream_ptr(stream)), "gla_workspace_init")
+    ws, nws = _ws(workspace, workspace.device)
+    with _on_device(workspace.device):
+        st = load().gla_workspace_init(ws, nws, _stream_ptr(stream))
+    _check(st, "gla_workspace_init")
 
 
 def workspace_error(workspace: torch.Tensor) -> int:
@@ -154,10 +156,34 @@ def workspace_error(workspace: torch.Tensor) -> int:
     return int(workspace[:4].view(torch.int32).item())
 
 
+def _ws(workspace: torch.Tensor, device):
+    """(pointer, size in bytes) of a workspace: a contiguous device tensor on
+    the inputs' device, of any dtype."""
+    if not workspace.is_cuda or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _out(out: Optional[torch.Tensor], shape, dtype, device) -> torch.Tensor:
+    """The caller's output tensor, checked (the kernels write all of it), or
+    a new one."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype or out.device != device or \
+            not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+    return out
+
+
+def _on_device(device):
+    """Calls run on the inputs' device (its current stream unless one is given)."""
+    return torch.cuda.device(device)
+
+
 def _shapes(q, k, v, gk, grid_h, grid_w):
     for name, t in (("q", q), ("k", k), ("v", v), ("gk", gk)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a device tensor on q's device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [B, T, H, D]")
         if t.dim() != 4:
@@ -180,26 +206,27 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
         stream: Optional[torch.cuda.Stream] = None, schedule: int = SCHED_AUTO) -> torch.Tensor:
     """o = key-only GLA forward along `direction` (int, or one per batch element)."""
     B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
-    if out is None:
-        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    out = _out(out, (B, T, H, dv), q.dtype, q.device)
     if workspace is None:
         workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
     if schedule == SCHED_AUTO:
-        st = load().gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
-                            out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
-                            chunk, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
-                            _stream_ptr(stream))
+        ws, nws = _ws(workspace, q.device)
+        with _on_device(q.device):
+            st = load().gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                                out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
+                                chunk, _dtype_code(q), ws, nws, _stream_ptr(stream))
         _check(st, "gla_fwd")
         return out
     return fwd_state(q, k, v, gk, grid_h, grid_w, direction, chunk, return_state=False, out=out,
                      workspace=workspace, stream=stream, schedule=schedule)
 
 
-def _state_ptr(t: Optional[torch.Tensor], B, H, dk, dv, name) -> Optional[int]:
+def _state_ptr(t: Optional[torch.Tensor], B, H, dk, dv, name, device=None) -> Optional[int]:
     if t is None:
         return None
-    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or \
+            (device is not None and t.device != device):
+        raise ValueError(f"{name} must be a contiguous float32 tensor on the inputs' device")
     if tuple(t.shape) != (B, H, dk, dv):
         raise ValueError(f"{name} must be [B, H, dk, dv] = {(B, H, dk, dv)}, got {tuple(t.shape)}")
     return t.data_ptr()
@@ -215,18 +242,19 @@ def fwd_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tenso
     zero); returns (o, S_T) with S_T written into s_final (allocated if None)
     when return_state, else o. schedule picks the kernel schedule."""
     B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
-    if out is None:
-        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    out = _out(out, (B, T, H, dv), q.dtype, q.device)
     if return_state and s_final is None:
         s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
-    st = load().gla_fwd_schedule(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
-                                 out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
-                                 _dirs(direction, B), chunk, _dtype_code(q),
-                                 _state_ptr(s0, B, H, dk, dv, "s0"),
-                                 _state_ptr(s_final, B, H, dk, dv, "s_final"), schedule,
-                                 workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    ws, nws = _ws(workspace, q.device)
+    p0 = _state_ptr(s0, B, H, dk, dv, "s0", q.device)
+    pf = _state_ptr(s_final, B, H, dk, dv, "s_final", q.device)
+    with _on_device(q.device):
+        st = load().gla_fwd_schedule(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                                     out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
+                                     _dirs(direction, B), chunk, _dtype_code(q), p0, pf, schedule,
+                                     ws, nws, _stream_ptr(stream))
     _check(st, "gla_fwd_schedule")
     return (out, s_final) if return_state else out
 
@@ -242,21 +270,23 @@ def fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tenso
     dtype, norm_weight [dv] float32."""
     B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
     if gate.shape != v.shape or gate.dtype != q.dtype or not gate.is_contiguous() or \
-            not gate.is_cuda:
-        raise ValueError("gate must be a contiguous device tensor shaped like v, in q's dtype")
+            gate.device != q.device:
+        raise ValueError("gate must be a contiguous tensor shaped like v, in q's dtype and on its device")
     if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (dv,) or \
-            not norm_weight.is_cuda or not norm_weight.is_contiguous():
-        raise ValueError("norm_weight must be a contiguous float32 [dv] device tensor")
-    if out is None:
-        out = torch.empty_like(v)
+            norm_weight.device != q.device or not norm_weight.is_contiguous():
+        raise ValueError("norm_weight must be a contiguous float32 [dv] tensor on q's device")
+    out = _out(out, (B, T, H, dv), q.dtype, q.device)
     if workspace is None:
         workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, q.device)
-    st = load().gla_fwd_gated(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
-                              gate.data_ptr(), norm_weight.data_ptr(), float(eps),
-                              out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
-                              chunk, _dtype_code(q), _state_ptr(s0, B, H, dk, dv, "s0"),
-                              _state_ptr(s_final, B, H, dk, dv, "s_final"), workspace.data_ptr(),
-                              workspace.numel(), _stream_ptr(stream))
+    ws, nws = _ws(workspace, q.device)
+    p0 = _state_ptr(s0, B, H, dk, dv, "s0", q.device)
+    pf = _state_ptr(s_final, B, H, dk, dv, "s_final", q.device)
+    with _on_device(q.device):
+        st = load().gla_fwd_gated(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                                  gate.data_ptr(), norm_weight.data_ptr(), float(eps),
+                                  out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
+                                  _dirs(direction, B), chunk, _dtype_code(q), p0, pf, ws, nws,
+                                  _stream_ptr(stream))
     _check(st, "gla_fwd_gated")
     return out
 
@@ -267,19 +297,23 @@ def chunk_summaries(k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspace
     B, T, H, dk, dv = _shapes(k, k, v, gk, grid_h, grid_w)
     if workspace is None:
         workspace = alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk, k.device)
-    st = load().gla_chunk_summaries(k.data_ptr(), v.data_ptr(), gk.data_ptr(), B, H, grid_h,
-                                    grid_w, dk, dv, _dirs(direction, B), chunk, _dtype_code(k),
-                                    workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    ws, nws = _ws(workspace, k.device)
+    with _on_device(k.device):
+        st = load().gla_chunk_summaries(k.data_ptr(), v.data_ptr(), gk.data_ptr(), B, H, grid_h,
+                                        grid_w, dk, dv, _dirs(direction, B), chunk, _dtype_code(k),
+                                        ws, nws, _stream_ptr(stream))
     _check(st, "gla_chunk_summaries")
     return workspace
 
 
 def state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace, s0=None, s_final=None,
                stream=None) -> torch.Tensor:
-    st = load().gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk,
-                               _state_ptr(s0, B, H, dk, dv, "s0"),
-                               _state_ptr(s_final, B, H, dk, dv, "s_final"),
-                               workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    ws, nws = _ws(workspace, workspace.device)
+    p0 = _state_ptr(s0, B, H, dk, dv, "s0", workspace.device)
+    pf = _state_ptr(s_final, B, H, dk, dv, "s_final", workspace.device)
+    with _on_device(workspace.device):
+        st = load().gla_state_scan(B, H, grid_h, grid_w, dk, dv, chunk, p0, pf, ws, nws,
+                                   _stream_ptr(stream))
     _check(st, "gla_state_scan")
     return workspace
 
@@ -287,12 +321,15 @@ def state_scan(B, H, grid_h, grid_w, dk, dv, chunk, workspace, s0=None, s_final=
 def chunk_outputs(q, k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspace=None,
                   out=None, stream=None) -> torch.Tensor:
     B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
-    if out is None:
-        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
-    st = load().gla_chunk_outputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
-                                  out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
-                                  _dirs(direction, B), chunk, _dtype_code(q),
-                                  workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    out = _out(out, (B, T, H, dv), q.dtype, q.device)
+    if workspace is None:
+        raise ValueError("chunk_outputs needs the workspace that holds the entering states")
+    ws, nws = _ws(workspace, q.device)
+    with _on_device(q.device):
+        st = load().gla_chunk_outputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                                      out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
+                                      _dirs(direction, B), chunk, _dtype_code(q), ws, nws,
+                                      _stream_ptr(stream))
     _check(st, "gla_chunk_outputs")
     return out
 
@@ -311,7 +348,8 @@ def workspace_views(workspace: torch.Tensor, B, H, grid_h, grid_w, dk, dv, chunk
 def scan_perm(grid_h: int, grid_w: int, direction: int, device="cuda", stream=None) -> torch.Tensor:
     """Device-computed scan order (raster index per scan position), int32."""
     perm = torch.empty(max(1, grid_h * grid_w), dtype=torch.int32, device=device)
-    st = load().gla_scan_perm(perm.data_ptr(), grid_h, grid_w, direction, _stream_ptr(stream))
+    with _on_device(perm.device):
+        st = load().gla_scan_perm(perm.data_ptr(), grid_h, grid_w, direction, _stream_ptr(stream))
     _check(st, "gla_scan_perm")
     return perm[:grid_h * grid_w]
 
@@ -322,23 +360,23 @@ def spatial_swiglu(a: torch.Tensor, u: torch.Tensor, weight: torch.Tensor,
     """h = silu(a) * (3x3 depthwise conv of u on the grid + bias); a, u [B, T, F]
     (float16 or float32, contiguous), weight [F, 3, 3] and bias [F] float32."""
     for name, t in (("a", a), ("u", u)):
-        if not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
-            raise ValueError(f"{name} must be a contiguous [B, T, F] device tensor")
+        if not t.is_cuda or t.device != u.device or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous [B, T, F] device tensor on u's device")
     if a.shape != u.shape or a.dtype != u.dtype:
         raise ValueError("a and u must share shape and dtype")
     B, T, Fc = u.shape
     if T != grid_h * grid_w:
         raise ValueError(f"T={T} but grid is {grid_h}x{grid_w}")
     if weight.dtype != torch.float32 or tuple(weight.shape) != (Fc, 3, 3) or \
-            not weight.is_contiguous() or not weight.is_cuda:
-        raise ValueError("weight must be a contiguous float32 [F, 3, 3] device tensor")
+            not weight.is_contiguous() or weight.device != u.device:
+        raise ValueError("weight must be a contiguous float32 [F, 3, 3] tensor on u's device")
     if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (Fc,)
-                             or not bias.is_cuda):
-        raise ValueError("bias must be a float32 [F] device tensor")
-    if out is None:
-        out = torch.empty_like(u)
-    st = load().gla_spatial_swiglu(a.data_ptr(), u.data_ptr(), weight.data_ptr(),
-                                   None if bias is None else bias.data_ptr(), out.data_ptr(),
-                                   B, grid_h, grid_w, Fc, _dtype_code(u), _stream_ptr(stream))
+                             or bias.device != u.device or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [F] tensor on u's device")
+    out = _out(out, tuple(u.shape), u.dtype, u.device)
+    with _on_device(u.device):
+        st = load().gla_spatial_swiglu(a.data_ptr(), u.data_ptr(), weight.data_ptr(),
+                                       None if bias is None else bias.data_ptr(), out.data_ptr(),
+                                       B, grid_h, grid_w, Fc, _dtype_code(u), _stream_ptr(stream))
     _check(st, "gla_spatial_swiglu")
     return out
