@@ -434,7 +434,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; there is no multi-GPU path "
+        print("bench.py: this implementation runs on one GPU only; there is no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
