@@ -167,6 +167,15 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
 // over all 16 segments, applied to S_0) is optionally written in fp32.
 // ===========================================================================
 constexpr int kScanSegs = 16;  // segments per chain: the lanes of a DPP row
+// The serial scan below replaces the segmented one from this many state
+// element groups of 8 per launch (B H dk dv / 8), or from half as many for
+// chains of 256 chunks and more. Measured on MI355X (64/64, graph-replayed):
+//   groups   N=25            N=100            N=256     (segmented / serial, us)
+//    8,192   3.6 / 4.9       7.7 / 12.2
+//   16,384   4.8 / 5.3      13.1 / 14.6      38.3 / 30.5
+//   32,768   7.4 / 5.9      22.3 / 16.8
+constexpr long kSerialScanGroups = 32768;
+constexpr int kSerialScanLongChain = 256;
 
 // R: chunks per segment kept in registers (2, 4 or 8, the segment length
 // rounded up, so that the clamped loads of a short segment are not repeated)
@@ -263,6 +272,60 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
   }
 }
 
+// The boundary scan for many chains at once: one thread per state element
+// group of 8, walking its chain's chunks in order with the loads of the next
+// W chunks in flight. A wave's load of one chunk covers 1 KB of contiguous
+// state (the segmented scan above touches 16 chunks in 64-byte pieces per
+// load and makes two dependent memory round trips per workgroup); with
+// enough chains the loads in flight cover the HBM latency, and each element
+// follows the recurrence S_{n+1} = a_n S_n + U_n exactly in order.
+template <int W>
+__global__ __launch_bounds__(kThreads) void scan_serial_kernel(const half_t* __restrict__ Uws,
+                                                               const float* __restrict__ Aws,
+                                                               half_t* __restrict__ Sws,
+                                                               const float* __restrict__ s0,
+                                                               float* __restrict__ sfin, int N,
+                                                               int DK, int DV, long groups) {
+  const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= groups) return;
+  const long DKDV = (long)DK * DV, per = DKDV / 8;
+  const long bh = gid / per;
+  const int x8 = 8 * (int)(gid - bh * per), d = x8 / DV;
+  const half_t* U = Uws + bh * N * DKDV + x8;
+  const float* A = Aws + bh * N * DK + d;
+  half_t* S = Sws + bh * N * DKDV + x8;
+  float s[8];
+  if (s0) {
+    load_f8(s0 + bh * DKDV + x8, s);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] = 0.f;
+  }
+  half8 u[W];
+  float a[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const long m = i < N ? i : N - 1;
+    u[i] = *reinterpret_cast<const half8*>(U + m * DKDV);
+    a[i] = A[m * DK];
+  }
+  for (int n0 = 0; n0 < N; n0 += W) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const int n = n0 + i;
+      if (n < N) {
+        store8(S + n * DKDV, s);  // the state entering chunk n
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = a[i] * s[c] + (float)u[i][c];
+      }
+      const long m = n + W < N ? n + W : N - 1;  // refill the slot (clamped)
+      u[i] = *reinterpret_cast<const half8*>(U + m * DKDV);
+      a[i] = A[m * DK];
+    }
+  }
+  if (sfin) store_f8(sfin + bh * DKDV + x8, s);
+}
+
 __global__ void scan_perm_kernel(int32_t* perm, int T, int gh, int gw, int dir) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t < T) perm[t] = scan_to_raster(t, T, gh, gw, dir);
@@ -336,6 +399,17 @@ hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* 
   const int L = (p.N + kScanSegs - 1) / kScanSegs;
   // 16 element groups of 8 per workgroup; dk*dv is a multiple of 1024
   dim3 grid((unsigned)(dkdv / (8 * (kThreads / kScanSegs))), p.H, nb);
+  const long groups = (long)nb * p.H * (dkdv / 8);
+  if (groups >= kSerialScanGroups || (groups >= kSerialScanGroups / 2 && p.N >= kSerialScanLongChain)) {
+    auto serial = p.N >= 64 ? scan_serial_kernel<16> : scan_serial_kernel<8>;
+    hipLaunchKernelGGL(serial, dim3((unsigned)((groups + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, s, reinterpret_cast<const half_t*>(ws + w.off_U) + bhn * dkdv,
+                       reinterpret_cast<const float*>(ws + w.off_a) + bhn * p.dk,
+                       reinterpret_cast<half_t*>(ws + w.off_S) + bhn * dkdv,
+                       s0 ? s0 + st : nullptr, sfin ? sfin + st : nullptr, p.N, p.dk, p.dv,
+                       groups);
+    return hipGetLastError();
+  }
   auto kernel = L <= 2 ? scan_kernel<2> : L <= 4 ? scan_kernel<4> : scan_kernel<8>;
   hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s,
                      reinterpret_cast<const half_t*>(ws + w.off_U) + bhn * dkdv,

@@ -129,3 +129,34 @@ def test_scan_phase_with_state_matches_chunked_model():
     _, _, _, S_ref, sT_ref = oracle.chunkwise(s(q), s(k), s(v), s(g), C, return_states=True, s0=s0)
     assert rel_err(S, S_ref) <= 2e-3
     assert rel_err(sf.double().cpu().numpy(), sT_ref) <= 2e-3
+
+
+@pytest.mark.parametrize("B,H,gh,gw,dk,dv,chunk", [
+    (8, 8, 16, 16, 64, 64, 16),    # 32,768 state groups, chains of 16 chunks (window 8)
+    (8, 8, 32, 32, 64, 64, 16),    # chains of 64 chunks (window 16)
+    (16, 16, 8, 8, 32, 32, 16),    # 32/32 heads, chains of 4 chunks (shorter than the window)
+    (4, 8, 64, 64, 64, 64, 16),    # 16,384 groups with chains of 256 chunks
+])
+def test_serial_scan_with_carried_state(B, H, gh, gw, dk, dv, chunk):
+    """Enough chains for the serial boundary scan: outputs and S_T against the
+    oracle, and the scan's entering states against the chunked model."""
+    q, k, v, g = W.make_inputs(B, gh * gw, H, dk, dv, np.float16, seed=350 + B + gh + dk)
+    s0 = _state(np.random.default_rng(8), B, H, dk, dv)
+    dirs = [b % 4 for b in range(B)]
+    say(f"serial scan B={B} H={H} grid={gh}x{gw} dk={dk} dv={dv} chunk={chunk}")
+    tq, tk, tv, tg = to_dev(q, k, v, g)
+    ts0 = to_dev(s0)[0]
+    o, sT = gla.fwd_state(tq, tk, tv, tg, gh, gw, dirs, chunk=chunk, s0=ts0,
+                          schedule=gla.SCHED_THREE_PHASE)
+    torch.cuda.synchronize()
+    ro, rs = oracle.gla_forward(q, k, v, g, gh, gw, dirs, s0=s0, return_state=True)
+    eo, es = rel_err(o.double().cpu().numpy(), ro), rel_err(sT.double().cpu().numpy(), rs)
+    say(f"  o err {eo:.2e}  S_T err {es:.2e}")
+    assert eo <= TOL and es <= TOL
+    ws = gla.chunk_summaries(tk, tv, tg, gh, gw, dirs, chunk)
+    gla.state_scan(B, H, gh, gw, dk, dv, chunk, ws, s0=ts0)
+    torch.cuda.synchronize()
+    _, _, S = (x.double().cpu().numpy() for x in gla.workspace_views(ws, B, H, gh, gw, dk, dv, chunk))
+    s = lambda x: oracle.to_scan(x, gh, gw, dirs)
+    _, _, _, S_ref, _ = oracle.chunkwise(s(q), s(k), s(v), s(g), chunk, return_states=True, s0=s0)
+    assert rel_err(S, S_ref) <= 2e-3
