@@ -47,7 +47,7 @@
  * segments, whose last chunks publish segment aggregates), and adds the
  * readout. Workgroups run in chain-major order and only wait on earlier
  * ones, with bounded waits. gla_fwd picks the single pass for chains of at
- * most 32 chunks, and for chains of at most 64 chunks on grids of at most 512
+ * most 32 chunks, and for chains of at most 56 chunks on grids of at most 512
  * chunk-heads (in both cases if the launch fits its control words), and the
  * three phases otherwise.
  *

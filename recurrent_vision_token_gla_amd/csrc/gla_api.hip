@@ -71,12 +71,13 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
 
 // Auto dispatch: the single pass saves two kernel boundaries and one read of
 // k, v, gk, but every chunk reads O(sqrt(N)) published tiles. Measured on
-// MI355X (64/64, chunk 64) it is ahead at every grid size tried for chains of
-// up to 25 chunks (to 12,288 chunk-heads), ahead at a few hundred chunk-heads
-// for chains of 49 and 64 chunks and behind at 1,500 and more, and behind
-// for chains of 100 chunks and longer.
+// MI355X (64/64, chunk 64, graph-replayed) it is ahead or within a few
+// percent for chains of up to 25 chunks at every grid tried (to 12,288
+// chunk-heads), ahead at a few hundred chunk-heads for chains of 49 chunks
+// (16.9 against 18.4 us) and behind for chains of 64 (20.1 against 18.9) and
+// longer, and behind at 1,500 chunk-heads and more for chains of 49.
 constexpr int kOnepassAnyGrid = 32;      // chains this short: single pass at any grid
-constexpr int kOnepassMaxChain = 64;     // up to here: on small grids only
+constexpr int kOnepassMaxChain = 56;     // up to here: on small grids only
 constexpr long kOnepassMaxChunks = 512;  // chunk-heads of such a small grid
 
 bool single_pass_fits(const gla::Problem& p) {

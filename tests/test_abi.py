@@ -160,11 +160,13 @@ def test_schedule_and_workspace_init_validate(lib):
 
 def test_auto_schedule(lib):
     # chains of 25 chunks: single pass at any grid; 49: on small grids only;
+    # 64: three phases;
     # 100: three phases; 4097 chunks: three phases
     assert gla.auto_schedule(1, 6, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
     assert gla.auto_schedule(4, 6, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
     assert gla.auto_schedule(8, 12, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
     assert gla.auto_schedule(1, 6, 56, 56, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    assert gla.auto_schedule(1, 6, 64, 64, 64, 64, 64) == gla.SCHED_THREE_PHASE
     assert gla.auto_schedule(4, 12, 56, 56, 64, 64, 64) == gla.SCHED_THREE_PHASE
     assert gla.auto_schedule(1, 6, 80, 80, 64, 64, 64) == gla.SCHED_THREE_PHASE
     assert gla.auto_schedule(4, 16, 80, 80, 64, 64, 64) == gla.SCHED_THREE_PHASE
