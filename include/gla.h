@@ -23,8 +23,8 @@
  *                           total decay a_n and its state contribution U_n;
  *   2. boundary scan     -- S_{n+1} = diag(a_n) S_n + U_n along the chunks;
  *   3. chunk outputs     -- for every (chunk, head) in parallel: the causal
- *                           intra-chunk decayed score tile (held in LDS)
- *                           times V, plus the readout of S_n.
+ *                           intra-chunk decayed score tile times V, plus the
+ *                           readout of S_n.
  *
  * Memory layout (all tensors caller-owned device memory, contiguous,
  * row-major, raster token order):
@@ -34,6 +34,18 @@
  * Accumulation is float in both cases. Supported: dk, dv in {32, 64},
  * chunk in {16, 32, 64}. Device pointers must be 16-byte aligned; the
  * workspace 256-byte aligned.
+ *
+ * Value range: any finite half inputs (|x| <= 65504) with gk <= 0. Every
+ * factor the kernels feed to a half-precision product has magnitude at most
+ * that of the q, k or v element it scales; where the exact diagonal of a
+ * chunk's score tile would need a larger factor, the kernels switch to float
+ * operands or to a direct float sum (chosen per 16-token block from the
+ * block's decay range and the magnitudes of its q and k rows). The state
+ * summaries, boundary states and score blocks are held in half with a
+ * power-of-two scale per row or block, so they have float's range. For
+ * GLA_F32 inputs, |q|, |k| and |v| must not exceed 65504 (they are rounded
+ * to half). An output whose exact value lies beyond the half range is +-Inf
+ * in GLA_F16.
  *
  * Directions: `dir` is a HOST array of B codes (GLA_L2R..GLA_B2T), one per
  * batch element; pass B copies for a single direction. Left->right is the
@@ -46,24 +58,29 @@
  * from the summaries its predecessors publish (grouped in about sqrt(N)
  * segments, whose last chunks publish segment aggregates), and adds the
  * readout. Workgroups run in chain-major order and only wait on earlier
- * ones, with bounded waits. gla_fwd picks the single pass for chains of at
- * most 32 chunks, and for chains of at most 56 chunks on grids of at most 512
- * chunk-heads (in both cases if the launch fits its control words), and the
- * three phases otherwise.
+ * ones, with bounded waits. gla_fwd_schedule and gla_auto_schedule say which
+ * one a call takes.
  *
  * Workspace: caller-owned device memory of gla_fwd_workspace_bytes bytes,
- * 256-byte aligned. Its first 64 KiB are control words of the single pass;
- * they must be ZERO before the workspace is first used (gla_workspace_init,
- * or any zero fill), and every call leaves them zero again, also when the
- * workspace is later used for another problem size. Word 0 is a sticky
- * error word: bit 0 set means a single-pass wait ran out of its poll budget
- * (results of that call are invalid); gla_workspace_init clears it.
+ * 256-byte aligned, of ANY contents. Its first 64 KiB are the single pass's
+ * control words. The single pass runs only on a workspace that
+ * gla_workspace_init has prepared: the library records the prepared start
+ * addresses, and every single-pass call leaves the words zero again (also
+ * across problem sizes). A workspace that was not prepared runs the three
+ * phases, which need no control words, so a plain allocation is always
+ * valid. If prepared memory is freed or written by anything other than this
+ * library, call gla_workspace_release (or gla_workspace_init again) first.
+ * Word 0 is a sticky error word: bit 0 set means a single-pass wait ran out
+ * of its poll budget (the results of that call are invalid);
+ * gla_workspace_status reads and clears it.
  *
  * Execution: asynchronous on `stream` (a hipStream_t passed as void*; NULL
- * is the default stream). No call allocates, synchronises or reads device
- * memory on the host, so every call can be captured in a HIP graph. Calls
- * are stateless and may run concurrently on different workspaces (never on
- * one workspace). The library keeps no pointer after a call returns.
+ * is the default stream). No forward call allocates, synchronises or reads
+ * device memory on the host, so every forward can be captured in a HIP
+ * graph (gla_workspace_status alone synchronises). Calls may run
+ * concurrently on different workspaces (never on one workspace). The library
+ * keeps no pointer after a call returns, except the addresses of prepared
+ * workspaces.
  *
  * Errors: arguments are checked on the host before any HIP call; a failing
  * check returns a negative status and touches nothing. A failed launch
@@ -90,38 +107,65 @@ enum {
   GLA_E_ARG = -1,          /* null/misaligned pointer, negative size, bad code */
   GLA_E_UNSUPPORTED = -2,  /* dk, dv or chunk outside the supported set */
   GLA_E_WORKSPACE = -3,    /* workspace smaller than gla_fwd_workspace_bytes */
-  GLA_E_HIP = -4           /* a HIP launch failed; see gla_last_error_detail */
+  GLA_E_HIP = -4,          /* a HIP launch failed; see gla_last_error_detail */
+  GLA_E_UNPREPARED = -5    /* single pass asked for on an unprepared workspace */
 };
 
 /* Library ABI version (incremented on any signature or layout change). */
 int gla_abi_version(void);
 
-/* Zero the workspace's control words (its first 64 KiB) with a kernel on
- * `stream` (graph-capturable). Needed once per workspace before its first
- * use; also clears the sticky error word. workspace_bytes is the size of the
- * buffer (at least 64 KiB). */
+/* Prepare a workspace for the single pass: zero its control words (its first
+ * 64 KiB, including the sticky error word) with a kernel on `stream`
+ * (graph-capturable) and record its start address as prepared.
+ * workspace_bytes is the size of the buffer (at least 64 KiB). */
 int gla_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forget that a workspace was prepared (call before freeing it or using its
+ * memory for anything else). Later forwards on it run the three phases
+ * until it is prepared again. GLA_E_ARG for NULL. */
+int gla_workspace_release(const void* workspace);
+
+/* 1 if gla_workspace_init prepared this start address (and it was not
+ * released since), else 0. */
+int gla_workspace_is_prepared(const void* workspace);
+
+/* Waits for the work queued on `stream`, then stores the workspace's sticky
+ * error word in *error_bits (bit 0: a single-pass wait ran out, the results
+ * of that call are invalid) and, if `clear` is nonzero, zeroes it.
+ * Synchronises, so it cannot be captured in a graph. GLA_E_WORKSPACE if
+ * workspace_bytes < 64 KiB; GLA_E_HIP if the copy fails. */
+int gla_workspace_status(void* workspace, size_t workspace_bytes,
+                         uint32_t* error_bits, int clear, void* stream);
+
 /* Bytes of workspace gla_fwd needs for this problem (0 for an empty one, or
- * if the shape is unsupported or negative). */
+ * if the shape is unsupported or negative). The workspace may hold anything
+ * on entry (see "Workspace" above for the prepared single-pass case). */
 size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk,
                                int dv, int chunk);
 
-/* Byte offsets, within the workspace, of the three intermediate arrays, so
- * that callers (tests) can inspect them after the phase calls below:
- *   U : half  [B][H][N][dk][dv]   chunk summaries (both schedules)
- *   a : float [B][H][N][dk]       per-chunk total decay exp(sum of gk)
+/* Byte offsets, within the workspace, of the intermediate arrays, so that
+ * callers (tests) can inspect them after the phase calls below:
+ *   U : half  [B][H][N][dk][dv]   chunk summaries (both schedules), row d
+ *                                 stored divided by its scale sigU
+ *   a : float [B][H][N][dk][2]    pairs (a_n[d], sigU_n[d]): the per-chunk
+ *                                 total decay exp(sum of gk) and the scale
+ *                                 of U_n row d
  *   S : half  [B][H][N][dk][dv]   state entering each chunk (three phases;
- *                                 the single pass keeps segment aggregates)
- * with N = ceil(T / chunk). Returns GLA_OK or GLA_E_ARG/GLA_E_UNSUPPORTED. */
+ *                                 the single pass keeps segment aggregates),
+ *                                 row d stored divided by its scale sigS
+ *   scales : float [B][H][N][dk]  sigS_n[d], at off_scales
+ * Scales are exact powers of two >= 1 (1 unless the row's magnitude passes
+ * 2^14); the stored row times its scale is the value. N = ceil(T / chunk).
+ * Returns GLA_OK or GLA_E_ARG/GLA_E_UNSUPPORTED. */
 int gla_workspace_layout(int B, int H, int grid_h, int grid_w, int dk, int dv,
                          int chunk, size_t* off_U, size_t* off_a,
-                         size_t* off_S, size_t* total_bytes);
+                         size_t* off_S, size_t* off_scales,
+                         size_t* total_bytes);
 
 /* The whole forward: o = GLA(q, k, v, gk) along dir[b] for each batch
- * element b (GTR project page, "A Kernel That Makes Recurrence Fast").
- * Enqueues the three phases below. o must not be the same buffer as any
- * input. */
+ * element b (GTR project page, "A Kernel That Makes Recurrence Fast"), on
+ * the schedule gla_auto_schedule names (the three phases on an unprepared
+ * workspace). o must not be the same buffer as any input. */
 int gla_fwd(const void* q, const void* k, const void* v, const void* gk,
             void* o, int B, int H, int grid_h, int grid_w, int dk, int dv,
             const int32_t* dir, int chunk, int dtype, void* workspace,
@@ -137,8 +181,9 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* gk,
  *   s_final : float [B][H][dk][dv], or NULL to skip the hand-back.
  * Both are in the scan's own frame (no spatial order); 16-byte aligned
  * device memory owned by the caller. s_final may be the same buffer as s0
- * (the state is then updated in place) but must not otherwise overlap s0,
- * the workspace or any tensor of the call. With both NULL this is gla_fwd. */
+ * (the state is then updated in place; such a call runs the three phases)
+ * but must not otherwise overlap s0 (GLA_E_ARG), the workspace or any
+ * tensor of the call. With both NULL this is gla_fwd. */
 int gla_fwd_state(const void* q, const void* k, const void* v, const void* gk,
                   void* o, int B, int H, int grid_h, int grid_w, int dk, int dv,
                   const int32_t* dir, int chunk, int dtype, const float* s0,
@@ -162,19 +207,20 @@ int gla_fwd_gated(const void* q, const void* k, const void* v, const void* gk,
                   void* stream);
 
 /* gla_fwd_state with an explicit schedule: GLA_SCHED_AUTO (what gla_fwd and
- * gla_fwd_state do), GLA_SCHED_SINGLE_PASS (returns GLA_E_UNSUPPORTED if the
- * problem does not fit its control words: more than 4096 chunks per chain,
- * or more chunk-heads per launch than the 64 KiB hold) or
- * GLA_SCHED_THREE_PHASE. Results agree up to rounding. */
+ * gla_fwd_state do), GLA_SCHED_SINGLE_PASS or GLA_SCHED_THREE_PHASE. The
+ * single pass returns GLA_E_UNPREPARED on a workspace gla_workspace_init has
+ * not prepared, and GLA_E_UNSUPPORTED if the problem does not fit its control
+ * words (more than 4096 chunks per chain, or more chunk-heads per launch than
+ * the 64 KiB hold) or if s_final is s0. Results agree up to rounding. */
 int gla_fwd_schedule(const void* q, const void* k, const void* v,
                      const void* gk, void* o, int B, int H, int grid_h,
                      int grid_w, int dk, int dv, const int32_t* dir, int chunk,
                      int dtype, const float* s0, float* s_final, int schedule,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* The schedule gla_fwd and gla_fwd_state take for this shape
- * (GLA_SCHED_SINGLE_PASS or GLA_SCHED_THREE_PHASE; the dtype does not
- * matter), or GLA_E_ARG / GLA_E_UNSUPPORTED for a bad shape. */
+/* The schedule gla_fwd and gla_fwd_state take for this shape on a prepared
+ * workspace (GLA_SCHED_SINGLE_PASS or GLA_SCHED_THREE_PHASE; the dtype does
+ * not matter), or GLA_E_ARG / GLA_E_UNSUPPORTED for a bad shape. */
 int gla_auto_schedule(int B, int H, int grid_h, int grid_w, int dk, int dv,
                       int chunk);
 
@@ -201,8 +247,8 @@ int gla_state_scan(int B, int H, int grid_h, int grid_w, int dk, int dv,
 /* Phase 3 alone: every chunk's outputs from its tokens and the workspace's
  * S: o_i = sum_{j<=i} A_ij v_j + (q_i * exp(b_i)) S_n with
  * A_ij = sum_d q_i[d] k_j[d] exp(b_i[d] - b_j[d]) (project page, "A Kernel
- * That Makes Recurrence Fast": the output kernel fuses the within-chunk
- * score-value product with the boundary-state readout). */
+ * That Makes Recurrence Fast": one output kernel takes both the in-chunk
+ * scores times values and the contribution of the entering state). */
 int gla_chunk_outputs(const void* q, const void* k, const void* v,
                       const void* gk, void* o, int B, int H, int grid_h,
                       int grid_w, int dk, int dv, const int32_t* dir,
@@ -217,9 +263,9 @@ int gla_scan_perm(int32_t* perm_dev, int grid_h, int grid_w, int dir,
                   void* stream);
 
 /* Spatial SwiGLU core: the channel mixer of a GTR block (ai.info summary of
- * GTR, "Methodology in Plain English"; project page, "How GTR Works") puts a
- * 3x3 depthwise convolution, on the 2-D patch grid, into the value branch of
- * a SwiGLU block. With the input projections already applied by the caller,
+ * GTR, "Methodology in Plain English"; project page, "How GTR Works"), a
+ * SwiGLU whose non-gated path is filtered per channel by a 3x3 kernel over
+ * the patch grid. With the input projections already applied by the caller,
  * a (gate branch) and u (value branch), this computes for every token (y, x)
  * of the grid and channel c
  *   h[y][x][c] = silu(a[y][x][c]) * (bias[c] +
@@ -238,7 +284,8 @@ int gla_spatial_swiglu(const void* a, const void* u, const float* weight,
 /* Static text for a status code; never NULL. */
 const char* gla_status_string(int status);
 
-/* Detail of the last GLA_E_HIP on the calling thread ("" if none). */
+/* Detail of the last GLA_E_HIP or GLA_E_UNPREPARED on the calling thread
+ * ("" if none). */
 const char* gla_last_error_detail(void);
 
 #ifdef __cplusplus

@@ -13,9 +13,9 @@ computed from the block input by the caller) and w a learned weight of dv
 values shared by the heads.
 
 Spatial SwiGLU (ai.info summary, "Methodology in Plain English"; project
-page, "How GTR Works"): a 3x3 depthwise convolution is inserted into the
-value branch of a SwiGLU block, applied on the 2-D patch grid and returned
-to sequence order. With a = W1 x (gate branch) and u = W3 x (value branch)
+page, "How GTR Works"): a SwiGLU mixer whose non-gated input path is
+filtered per channel by a 3x3 kernel over the 2-D patch grid before the
+gating product, with tokens back in sequence order afterwards. With a = W1 x (gate branch) and u = W3 x (value branch)
 already projected by the caller, per token (y, x) of the grid and channel c:
 
     h[y, x, c] = silu(a[y, x, c]) * (bias[c] + sum_{i, j in 0..2}

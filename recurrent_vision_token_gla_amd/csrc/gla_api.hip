@@ -6,12 +6,33 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "gla.h"
 #include "gla_launch.h"
 
 namespace {
 
 thread_local char g_detail[256] = "";
+
+// Workspaces whose control words gla_workspace_init has zeroed (start address
+// -> bytes). The single pass trusts those words only on such a workspace; any
+// other workspace runs the three phases, which read no control words, so a
+// workspace of arbitrary contents always gives correct results.
+std::mutex g_prepared_mu;
+std::unordered_map<uintptr_t, size_t> g_prepared;
+
+bool is_prepared(const void* ws) {
+  std::lock_guard<std::mutex> lk(g_prepared_mu);
+  const auto it = g_prepared.find(reinterpret_cast<uintptr_t>(ws));
+  return it != g_prepared.end() && it->second >= (size_t)gla::kCtrlWords * sizeof(unsigned);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
 
 int fail_hip(hipError_t e, const char* where) {
   snprintf(g_detail, sizeof(g_detail), "%s: %s", where, hipGetErrorString(e));
@@ -71,11 +92,13 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
 
 // Auto dispatch: the single pass saves two kernel boundaries and one read of
 // k, v, gk, but every chunk reads O(sqrt(N)) published tiles. Measured on
-// MI355X (64/64, chunk 64, graph-replayed) it is ahead or within a few
-// percent for chains of up to 25 chunks at every grid tried (to 12,288
-// chunk-heads), ahead at a few hundred chunk-heads for chains of 49 chunks
-// (16.9 against 18.4 us) and behind for chains of 64 (20.1 against 18.9) and
-// longer, and behind at 1,500 chunk-heads and more for chains of 49.
+// MI355X (64/64, chunk 64, graph-replayed), single pass against three phases:
+// chains of 25 chunks 12.9 vs 14.1 us at 150 chunk-heads, 45.9 vs 47.5 at
+// 2,400 and 221.9 vs 229.5 at 12,288, but 84.5 vs 82.8 at 4,800 and 115.9 vs
+// 103.6 at 6,144; chains of 49 chunks 16.9 vs 18.4 at 294 chunk-heads and
+// behind from about 2,400; chains of 64 chunks 20.1 vs 18.9 at 384. Chains
+// of 26 to 32 and 50 to 56 chunks were not measured: the limits below
+// interpolate between those points.
 constexpr int kOnepassAnyGrid = 32;      // chains this short: single pass at any grid
 constexpr int kOnepassMaxChain = 56;     // up to here: on small grids only
 constexpr long kOnepassMaxChunks = 512;  // chunk-heads of such a small grid
@@ -138,6 +161,10 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
     const void* sf = s_final;
     if (sf == q || sf == k || sf == v || sf == gk || sf == o || sf == workspace) return GLA_E_ARG;
   }
+  // s_final may be s0 (an in-place update) but must not otherwise overlap it
+  const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
+  const bool in_place = s0 && s_final && overlaps(s0, state_bytes, s_final, state_bytes);
+  if (in_place && (const void*)s0 != (const void*)s_final) return GLA_E_ARG;
   if (epi.gate) {
     GLA_TRY(check_tensor(epi.gate));
     if (!epi.weight || !aligned(epi.weight, 16)) return GLA_E_ARG;
@@ -145,8 +172,19 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
   }
   GLA_TRY(check_dirs(dir, B));
   GLA_TRY(check_ws(p, workspace, workspace_bytes));
-  bool onepass = single_pass_fits(p);
+  // In the single pass the chain's last chunk writes S_T while other chunks
+  // of the chain may still read s0, so an in-place update takes the three
+  // phases, whose scan reads each element of s0 before it writes the same
+  // element of s_final.
+  const bool prepared = is_prepared(workspace);
+  bool onepass = single_pass_fits(p) && !in_place;
   if (mode == 1 && !onepass) return GLA_E_UNSUPPORTED;
+  if (mode == 1 && !prepared) {
+    snprintf(g_detail, sizeof(g_detail),
+             "the single pass needs a workspace prepared by gla_workspace_init");
+    return GLA_E_UNPREPARED;
+  }
+  onepass = onepass && prepared;
   if (mode == 0) onepass = onepass && prefer_single_pass(p);
   if (mode == 2) onepass = false;
   if (onepass) {
@@ -171,7 +209,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
 
 extern "C" {
 
-int gla_abi_version(void) { return 4; }
+int gla_abi_version(void) { return 5; }
 
 size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk, int dv,
                                int chunk) {
@@ -184,15 +222,17 @@ size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk, int
 }
 
 int gla_workspace_layout(int B, int H, int grid_h, int grid_w, int dk, int dv, int chunk,
-                         size_t* off_U, size_t* off_a, size_t* off_S, size_t* total_bytes) {
+                         size_t* off_U, size_t* off_a, size_t* off_S, size_t* off_scales,
+                         size_t* total_bytes) {
   gla::Problem p;
   bool empty;
   GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, GLA_F16, &p, &empty));
-  if (!off_U || !off_a || !off_S || !total_bytes) return GLA_E_ARG;
+  if (!off_U || !off_a || !off_S || !off_scales || !total_bytes) return GLA_E_ARG;
   const gla::WsLayout w = gla::workspace_layout(p);
   *off_U = w.off_U;
   *off_a = w.off_a;
   *off_S = w.off_S;
+  *off_scales = w.off_ss;
   *total_bytes = empty ? 0 : w.total;
   return GLA_OK;
 }
@@ -303,6 +343,38 @@ int gla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   const hipError_t e =
       gla::launch_ctrl_clear(static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "workspace init launch");
+  std::lock_guard<std::mutex> lk(g_prepared_mu);
+  g_prepared[reinterpret_cast<uintptr_t>(workspace)] = workspace_bytes;
+  return GLA_OK;
+}
+
+int gla_workspace_release(const void* workspace) {
+  if (!workspace) return GLA_E_ARG;
+  std::lock_guard<std::mutex> lk(g_prepared_mu);
+  g_prepared.erase(reinterpret_cast<uintptr_t>(workspace));
+  return GLA_OK;
+}
+
+int gla_workspace_is_prepared(const void* workspace) {
+  return workspace && is_prepared(workspace) ? 1 : 0;
+}
+
+int gla_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* error_bits, int clear,
+                         void* stream) {
+  if (!workspace || !aligned(workspace, 256) || !error_bits) return GLA_E_ARG;
+  if (workspace_bytes < (size_t)gla::kCtrlWords * sizeof(unsigned)) return GLA_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail_hip(e, "workspace status read");
+  *error_bits = word;
+  if (clear && word != 0u) {
+    static const uint32_t zero = 0u;
+    e = hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail_hip(e, "workspace status clear");
+  }
   return GLA_OK;
 }
 
@@ -345,6 +417,7 @@ const char* gla_status_string(int status) {
     case GLA_E_UNSUPPORTED: return "GLA_E_UNSUPPORTED: dk, dv or chunk outside the supported set, or problem too large";
     case GLA_E_WORKSPACE: return "GLA_E_WORKSPACE: workspace smaller than gla_fwd_workspace_bytes()";
     case GLA_E_HIP: return "GLA_E_HIP: a HIP launch failed (see gla_last_error_detail)";
+    case GLA_E_UNPREPARED: return "GLA_E_UNPREPARED: the single pass needs a workspace prepared by gla_workspace_init";
     default: return "unknown GLA status";
   }
 }

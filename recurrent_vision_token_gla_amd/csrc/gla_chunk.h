@@ -28,9 +28,17 @@ namespace tile {
 //   off-diagonal J < I: A_IJ = (Q~_I * m_IJ) K~_J^T, m_IJ = 2^(beta_I - e_J)
 //   diagonal:           A_II = Q' K'^T with Q' = q 2^(s_i - s_7),
 //                       K' = k 2^(s_7 - s_j): one reference at the 8th token.
-// The diagonal block uses half operands when no key dim decays by more than
-// 2^8 over a sub-block, fp32 operands up to 2^120, and beyond that (checked
-// per tile) sums every entry directly from 2^(s_i - s_j).
+// Each wave picks the diagonal block's arithmetic from its own 16 tokens:
+// half operands while no key dim decays by more than 2^8 over the block and
+// max(|q|, |k|) * 2^range stays within 2^15, float operands while the range
+// is within 2^120 and those factors stay finite, and beyond that a direct
+// float sum of every entry from 2^(s_i - s_j). Score entries beyond 2^14 in
+// magnitude make the wave divide its score blocks by a power of two sigA,
+// undone on the accumulators (the product with V is linear).
+//
+// The three-phase entering state S_n arrives as half rows divided by their
+// power-of-two scales sigS[d] >= 1. The readout folds sigS[d] / max_d sigS
+// into Q^ (a factor <= 1) and multiplies the accumulators by max_d sigS.
 //
 // kFused = false: phase 3 of three; S_n comes from the boundary scan.
 // kFused = true: the whole forward in one pass (the chunk summary, the
@@ -49,11 +57,11 @@ namespace tile {
 //   3. adds the readout Q^ S_n and stores the outputs.
 // ===========================================================================
 template <int DK, int DV, int C, typename InT, bool kFused, bool kGate>
-__global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
+__global__ __launch_bounds__(kThreads, kFused ? 3 : 4) void chunk_kernel(
     const InT* __restrict__ qp, const InT* __restrict__ kp, const InT* __restrict__ vp,
     const InT* __restrict__ gp, InT* __restrict__ op, half_t* __restrict__ Uws,
-    float* __restrict__ Aws, half_t* __restrict__ Sws, float* __restrict__ GAws,
-    unsigned* __restrict__ ctrl, const float* __restrict__ s0, float* __restrict__ sfin,
+    float* __restrict__ Aws, half_t* __restrict__ Sws, const float* __restrict__ SigS,
+    float* __restrict__ GAws, unsigned* __restrict__ ctrl, const float* s0, float* sfin,
     const InT* __restrict__ zp, const float* __restrict__ nw, float eps, int T, int H, int N,
     int G, int nseg, int gh, int gw, DirPack dirs) {
   constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
@@ -91,7 +99,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __shared__ __attribute__((aligned(16))) float sF[kFused ? NB : 1][DK];  // K^ = K~ * sF
   __shared__ float sAn[kFused ? DK : 1];
   __shared__ int sRow[C];
-  __shared__ int sTier;
+  __shared__ float sSig[DK];  // row scales of S_n
+  __shared__ float sSigMax;
+  __shared__ unsigned sRowMax[kFused ? DK : 1];  // single pass: row maxima of U_n
+  __shared__ float sSigU[kFused ? DK : 1];       // single pass: row scales of U_n
+  __shared__ unsigned sSMax;                     // single pass: largest row scale of S_n
   __shared__ unsigned sDone, sPub;
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
@@ -129,7 +141,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // the row table (for the scatter) and the flags below are first read after
   // the barrier that follows the cumulative sums
   chunk_rows<C>(sRow, n * C, T, gh, gw, dir);
-  if (tid == 0) sTier = 0, sPub = 0u;
+  if (tid == 0) sPub = 0u, sSMax = 0u;
+  if (kFused && tid < DK) sRowMax[tid] = 0u;
 
   // -- this wave's token rows of q, k, gk in the operand layout (waves past
   // the last sub-block load a padding row too: no branch around the loads)
@@ -150,10 +163,12 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // issued before the first LDS write that waits on one
   constexpr int NSIT = kFused ? 1 : (DKDV / 8 + kThreads - 1) / kThreads;
   half8 h8[NSIT];
+  float sig_d = 1.f;  // thread d < DK: row scale of S_n row d
   if constexpr (!kFused) {
     const half_t* Sb = Sws + bhn * (long)DKDV;
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) h8[it] = load8h(Sb + 8 * ((tid + kThreads * it) % (DKDV / 8)));
+    sig_d = SigS[bhn * DK + (tid % DK)];
   }
   load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV);
   if constexpr (!kFused) {
@@ -165,6 +180,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         *reinterpret_cast<half8*>(&sS[d][e8]) = h8[it];
       }
     }
+    if (tid < DK) sSig[tid] = sig_d;
   }
 
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
@@ -201,7 +217,15 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       else if (J == I2) tot = tots[J];
       else after += tots[J];
     }
-    sEb[I2][d] = fexp2(beta);
+    if constexpr (kFused) {
+      sEb[I2][d] = fexp2(beta);
+    } else {
+      // Q^ factor 2^beta * sigS[d] / max sigS (the accumulators take max sigS)
+      const float sg = sSig[d];
+      const float smax = __any(sg != 1.f) ? group_max<DK>(sg) : 1.f;
+      if (tid == 0) sSigMax = smax;
+      sEb[I2][d] = fexp2(beta) * sg * inv_scale(smax);
+    }
     sR1[I2][d] = fexp2(-s7);
     sR2[I2][d] = fexp2(s7 - tot);
     float acc = 0.f;  // log2 of m_{I2,J} for J = I2-1, I2-2, ...
@@ -212,9 +236,6 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         acc += tots[J];
       }
     }
-    const float range = -tot;
-    if (!(range <= kF32Range)) atomicMax(&sTier, 2);
-    else if (!(range <= kHalfRange)) atomicMax(&sTier, 1);
     if constexpr (kFused) {
       sF[I2][d] = fexp2(after);
       if (I2 == NB - 1) sAn[d] = fexp2(beta + tot);  // a_n = 2^(chunk total)
@@ -224,11 +245,17 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // -- per-element factors; K~ goes to LDS for the other sub-blocks, and in
   // one pass K^ = K~ 2^(totals of the later sub-blocks), for U
   float qt[NEL], kt[NEL];
+  float rng = 0.f, big = 0.f;  // this lane's decay range (log2) and max(|q|, |k|)
   if (owner) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       float tt[8], ff[8];
       lds8(&sTot[I][32 * ks + lk], tt);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        rng = fmaxf(rng, -tt[c]);
+        big = fmaxf(big, fmaxf(fabsf(qf[8 * ks + c]), fabsf(kf[8 * ks + c])));
+      }
       if constexpr (kFused) lds8(&sF[I][32 * ks + lk], ff);
       half8 k8, kh8;
 #pragma unroll
@@ -267,6 +294,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
           const half4 bb = ld_tr<HSTR, 4>(&sKh[16 * J][16 * D]);
           uacc[i] = mfma16x16x16(a, bb, uacc[i]);
         }
+        const float m = fmaxf(fmaxf(fabsf(uacc[i][0]), fabsf(uacc[i][1])),
+                              fmaxf(fabsf(uacc[i][2]), fabsf(uacc[i][3])));
+        atomicMax(&sRowMax[16 * D + lr], __float_as_uint(m));
       }
     }
     __syncthreads();  // K^ is no longer read: the region becomes the U staging tile
@@ -275,19 +305,23 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       const int blk = wave + 4 * i;
       if (blk < NBLK) {
         const int E = blk / ND, D = blk % ND;
-        half4 hv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = (half_t)uacc[i][r];
-        *reinterpret_cast<half4*>(&sU[16 * D + lr][16 * E + 4 * lq]) = hv;
+        const float inv = inv_scale(row_scale(__uint_as_float(sRowMax[16 * D + lr])));
+        const floatx4 x = uacc[i] * inv;
+        *reinterpret_cast<half4*>(&sU[16 * D + lr][16 * E + 4 * lq]) = cvt4(x);
       }
     }
     __syncthreads();
-    // wave 0 alone stores and flags U_n and a_n, so that the other waves go
-    // on to their score blocks without waiting for the stores to complete
+    // wave 0 alone stores and flags U_n (rows divided by their scales), the
+    // row scales and a_n, so that the other waves go on to their score blocks
+    // without waiting for the stores to complete
     if (wave == 0) {
       for (int x8 = 8 * lane; x8 < DKDV; x8 += 8 * 64)
         st_coh(rU, n * DKDV + x8, *reinterpret_cast<const half8*>(&sU[x8 / DV][x8 % DV]));
-      for (int d = lane; d < DK; d += 64) st_dev(Aws + bhn * DK + d, sAn[d]);
+      for (int d = lane; d < DK; d += 64) {
+        const float sg = row_scale(__uint_as_float(sRowMax[d]));
+        sSigU[d] = sg;
+        st_dev2(Aws + 2 * (bhn * DK + d), sAn[d], sg);
+      }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (lane == 0) __hip_atomic_store(cw + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -295,8 +329,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 
   half4 A[NB];
   half8 qh[NKS];
+  float sigA = 1.f;  // this wave's score blocks are stored divided by sigA
   if (owner) {
-    const int tier = sTier;
+    // the diagonal operands are q 2^(s_i - s_7) and k 2^(s_7 - s_j), each
+    // at most max(|q|, |k|) 2^range in magnitude
+    const float amp = big * fexp2(fminf(rng, 127.f));
+    const int tier = __all(rng <= kHalfRange && amp <= 32768.f)  ? 0
+                     : __all(rng <= kF32Range && amp < 0x1p126f) ? 1
+                                                                  : 2;
     // -- diagonal sub-block, transposed: acc[r] = A[i = lr][j = 4*lq + r]
     floatx4 dacc = {0.f, 0.f, 0.f, 0.f};
     if (tier == 0) {
@@ -340,12 +380,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         if ((j >> 2) == lq) dacc[j & 3] = part;
       }
     }
-    half4 adiag;
+    floatx4 Af[NB];  // score blocks in float, before the cast to half
 #pragma unroll
-    for (int r = 0; r < 4; ++r) adiag[r] = (half_t)((4 * lq + r <= lr) ? dacc[r] : 0.f);
+    for (int r = 0; r < 4; ++r) dacc[r] = (4 * lq + r <= lr) ? dacc[r] : 0.f;
 #pragma unroll
-    for (int J = 0; J < NB; ++J)
-      if (J == I) A[J] = adiag;
+    for (int J = 0; J < NB; ++J) {
+      if (J == I) Af[J] = dacc;
+      else if (J > I) Af[J] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     // -- off-diagonal sub-blocks J < I
 #pragma unroll
     for (int J = 0; J < NB - 1; ++J) {
@@ -354,36 +396,62 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          float mm[8];
+          float mm[8], x[8];
           lds8(&sM[pr][32 * ks + lk], mm);
-          half8 qm;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) qm[c] = (half_t)(qt[8 * ks + c] * mm[c]);
+          for (int c = 0; c < 8; ++c) x[c] = qt[8 * ks + c] * mm[c];
           const half8 ka = *reinterpret_cast<const half8*>(&sKt[16 * J + lr][32 * ks + lk]);
-          acc = mfma16x16x32(ka, qm, acc);
+          acc = mfma16x16x32(ka, cvt8(x), acc);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) A[J][r] = (half_t)acc[r];
+        Af[J] = acc;
       }
     }
+    // -- entries beyond 2^14 (large q and k): divide the wave's blocks by a
+    // power of two, undone on the accumulators
+    float am = 0.f;
+#pragma unroll
+    for (int J = 0; J < NB; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(Af[J][r]));
+    if (__any(am > kRowRange)) {
+      sigA = row_scale(group_max<64>(am));
+      const float inv = inv_scale(sigA);
+#pragma unroll
+      for (int J = 0; J < NB; ++J) Af[J] *= inv;
+    }
+#pragma unroll
+    for (int J = 0; J < NB; ++J) A[J] = cvt4(Af[J]);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      float eb[8];
+      float eb[8], x[8];
       lds8(&sEb[I][32 * ks + lk], eb);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) qh[ks][c] = (half_t)(qt[8 * ks + c] * eb[c]);
+      for (int c = 0; c < 8; ++c) x[c] = qt[8 * ks + c] * eb[c];
+      qh[ks] = cvt8(x);
     }
   }
 
   if constexpr (!kFused) {
     __syncthreads();  // K~ is no longer read: its LDS becomes the output tile
-    // -- O_I = Q^_I S + sum_{J<=I} A_IJ V_J
+    // -- O_I = sum_{J<=I} A_IJ V_J + Q^_I S, with A stored / sigA and the
+    // readout taken / max sigS
     if (owner) {
+      const float smax = sSigMax;
+      const bool rescale = sigA != 1.f || smax != 1.f;
+      const float f1 = sigA * inv_scale(smax);
 #pragma unroll
       for (int E = 0; E < NE; ++E) {
         // one accumulation chain of a single product shape (16x16x16) per value
         // block: the readout contracts four key dims per lane group per step
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+          if (J <= I) {
+            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
+            acc = mfma16x16x16(A[J], vb, acc);
+          }
+        }
+        if (rescale) acc *= f1;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -394,13 +462,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             acc = mfma16x16x16(qa, sb, acc);
           }
         }
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J <= I) {
-            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
-            acc = mfma16x16x16(A[J], vb, acc);
-          }
-        }
+        if (rescale) acc *= smax;
         stage_out(acc, E);
       }
     }
@@ -420,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     // all groups' loads of a batch of predecessors go out together
     for (int m = n - 1; m >= n0; m -= LB) {
       half8 u[NGR][LB];
-      float a[NGR][LB];
+      float a[NGR][LB], su[NGR][LB];
 #pragma unroll
       for (int g = 0; g < NGR; ++g) {  // clamped, unconditional loads
         const int x8 = (8 * (tid + kThreads * g)) % DKDV;
@@ -428,7 +490,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         for (int j = 0; j < LB; ++j) {
           const int mj = m - j >= n0 ? m - j : n0;
           u[g][j] = ld_coh(rU, mj * DKDV + x8);
-          a[g][j] = ld_dev(Aws + (bh * N + mj) * DK + x8 / DV);
+          const float2 p = ld_dev2(Aws + 2 * ((bh * N + mj) * DK + x8 / DV));  // (a, sigU)
+          a[g][j] = p.x, su[g][j] = p.y;
         }
       }
 #pragma unroll
@@ -437,11 +500,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
           if (x8 < DKDV && m - j >= n0) {
+            const float w = wv[g] * su[g][j];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) xs[g][c] += wv[g] * (float)u[g][j][c];
+            for (int c = 0; c < 8; ++c) xs[g][c] += w * (float)u[g][j][c];
             wv[g] *= a[g][j];
           }
           consume(u[g][j], a[g][j]);
+          consume(u[g][j], su[g][j]);
         }
       }
     }
@@ -452,18 +517,22 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       for (int g = 0; g < NGR; ++g) {
         const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
         if (x8 < DKDV) {
-          half8 ag;
           const half8 un = *reinterpret_cast<const half8*>(&sU[d][x8 % DV]);  // own U_n
+          float ag[8], m = 0.f;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) ag[c] = (half_t)(sAn[d] * xs[g][c] + (float)un[c]);
-          st_coh(rS, seg * DKDV + x8, ag);
+          for (int c = 0; c < 8; ++c) {
+            ag[c] = sAn[d] * xs[g][c] + sSigU[d] * (float)un[c];
+            m = fmaxf(m, fabsf(ag[c]));
+          }
+          // the DV/8 neighbouring lanes of row d agree on its scale
+          const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
+          const float inv = inv_scale(sg);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) ag[c] *= inv;
+          st_coh(rS, seg * DKDV + x8, cvt8(ag));
+          // with the segment's decay: the weight the look-back accumulated, times a_n
+          if (x8 % DV == 0) st_dev2(GAws + 2 * (gs * DK + d), wv[g] * sAn[d], sg);
         }
-      }
-      // the segment's decay: the weight the look-back accumulated, times a_n
-#pragma unroll
-      for (int g = 0; g < NGR; ++g) {
-        const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
-        if (x8 < DKDV && x8 % DV == 0) st_dev(GAws + gs * DK + d, wv[g] * sAn[d]);
       }
     }
     // -- intra-chunk part, while the aggregate's stores complete and the
@@ -495,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     }
     for (int s2 = seg - 1; s2 >= 0; s2 -= LB) {
       half8 u[NGR][LB];
-      float a[NGR][LB];
+      float a[NGR][LB], su[NGR][LB];
 #pragma unroll
       for (int g = 0; g < NGR; ++g) {  // clamped, unconditional loads
         const int x8 = (8 * (tid + kThreads * g)) % DKDV;
@@ -503,7 +572,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         for (int j = 0; j < LB; ++j) {
           const int sj = s2 - j >= 0 ? s2 - j : 0;
           u[g][j] = ld_coh(rS, sj * DKDV + x8);
-          a[g][j] = ld_dev(GAws + (bh * nseg + sj) * DK + x8 / DV);
+          const float2 p = ld_dev2(GAws + 2 * ((bh * nseg + sj) * DK + x8 / DV));  // (decay, sig)
+          a[g][j] = p.x, su[g][j] = p.y;
         }
       }
 #pragma unroll
@@ -512,11 +582,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
           if (x8 < DKDV && s2 - j >= 0) {
+            const float w = w2[g] * su[g][j];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) pv[g][c] += w2[g] * (float)u[g][j][c];
+            for (int c = 0; c < 8; ++c) pv[g][c] += w * (float)u[g][j][c];
             w2[g] *= a[g][j];
           }
           consume(u[g][j], a[g][j]);
+          consume(u[g][j], su[g][j]);
         }
       }
     }
@@ -542,25 +614,53 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
           for (int c = 0; c < 8; ++c) pv[g][c] += w2[g] * z[c];
         }
+        float m = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) xs[g][c] += wv[g] * pv[g][c];  // S_n
+        for (int c = 0; c < 8; ++c) {
+          xs[g][c] += wv[g] * pv[g][c];  // S_n
+          m = fmaxf(m, fabsf(xs[g][c]));
+        }
         if (fin) {
           float f[8];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) f[c] = sAn[d] * xs[g][c] + (float)ul[g][c];
+          for (int c = 0; c < 8; ++c) f[c] = sAn[d] * xs[g][c] + sSigU[d] * (float)ul[g][c];
           store_f8(sfin + bh * DKDV + x8, f);
         }
-        half8 s8;
+        // S_n staged in half, row d divided by its scale
+        const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
+        const float inv = inv_scale(sg);
+        float o[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s8[c] = (half_t)xs[g][c];
-        *reinterpret_cast<half8*>(&sS[d][x8 % DV]) = s8;
+        for (int c = 0; c < 8; ++c) o[c] = xs[g][c] * inv;
+        *reinterpret_cast<half8*>(&sS[d][x8 % DV]) = cvt8(o);
+        if (x8 % DV == 0) {
+          sSig[d] = sg;
+          atomicMax(&sSMax, __float_as_uint(sg));
+        }
       }
     }
     __syncthreads();  // S_n complete in LDS; every read of published data done
-    // -- readout, on the same accumulation chains: O_I += Q^_I S_n
+    // -- readout, on the same accumulation chains: O_I += Q^_I S_n, with the
+    // row scales of S_n folded into Q^ (factors sigS[d] / max sigS <= 1) and
+    // the accumulators taken / max sigS meanwhile
     if (owner) {
+      const float smax = __uint_as_float(sSMax);
+      if (smax != 1.f) {
+        const float is = inv_scale(smax);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          float f[8], x[8];
+          lds8(&sSig[32 * ks + lk], f);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) x[c] = (float)qh[ks][c] * (f[c] * is);
+          qh[ks] = cvt8(x);
+        }
+      }
+      const bool rescale = sigA != 1.f || smax != 1.f;
+      const float f1 = sigA * inv_scale(smax);
 #pragma unroll
       for (int E = 0; E < NE; ++E) {
+        if (rescale) oacc[E] *= f1;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -571,6 +671,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             oacc[E] = mfma16x16x16(qa, sb, oacc[E]);
           }
         }
+        if (smax != 1.f) oacc[E] *= smax;
         stage_out(oacc[E], E);
       }
     }
@@ -649,6 +750,7 @@ hipError_t outputs_t(const Problem& p, int b0, int nb, const DirPack& dirs, cons
                      static_cast<InT*>(o) + tok * DV, nullptr, nullptr,
                      const_cast<half_t*>(reinterpret_cast<const half_t*>(ws + w.off_S)) +
                          bhn * DK * DV,
+                     reinterpret_cast<const float*>(ws + w.off_ss) + bhn * DK,
                      nullptr, nullptr, nullptr, nullptr,
                      kGate ? static_cast<const InT*>(epi.gate) + tok * DV : nullptr,
                      epi.weight, epi.eps, p.T, p.H, p.N, 1, 1, p.gh, p.gw, dirs);
@@ -672,9 +774,9 @@ hipError_t onepass_t(const Problem& p, int b0, int nb, const DirPack& dirs, cons
                      static_cast<const InT*>(v) + tok * DV, static_cast<const InT*>(gk) + tok * DK,
                      static_cast<InT*>(o) + tok * DV,
                      reinterpret_cast<half_t*>(ws + w.off_U) + bhn * DK * DV,
-                     reinterpret_cast<float*>(ws + w.off_a) + bhn * DK,
-                     reinterpret_cast<half_t*>(ws + w.off_S) + bhs * DK * DV,
-                     reinterpret_cast<float*>(ws + w.off_g) + bhs * DK,
+                     reinterpret_cast<float*>(ws + w.off_a) + 2 * bhn * DK,
+                     reinterpret_cast<half_t*>(ws + w.off_S) + bhs * DK * DV, nullptr,
+                     reinterpret_cast<float*>(ws + w.off_g) + 2 * bhs * DK,
                      reinterpret_cast<unsigned*>(ws), s0 ? s0 + st : nullptr,
                      sfin ? sfin + st : nullptr,
                      kGate ? static_cast<const InT*>(epi.gate) + tok * DV : nullptr, epi.weight,

@@ -33,13 +33,17 @@ namespace tile {
 // ===========================================================================
 // Phase 1: chunk summaries. One workgroup per (chunk n, head h, batch b).
 //   U[d][e] = sum_j K^[j][d] V[j][e],     K^[j] = k_j 2^(B - b_j)  (<= |k|)
-//   a[d]      = 2^(B[d])
+//   a[d]      = 2^(B[d]), stored as the pair (a[d], m[d]) with m[d] the
+//               largest |U[d][e]| (the scan's bound needs it; U's row scale
+//               is row_scale(m[d]))
 // Wave w owns the 16 tokens of sub-block w, one token per lane row, and
 // takes its cumulative decay with a DPP row scan plus the totals of the
 // earlier sub-blocks. K^ and V go to LDS as token rows (16-byte stores) and
 // both operands of the token contraction come back through the transposing
 // LDS read; U is produced (as U^T) in 16x16 blocks on the matrix cores,
-// staged through LDS as rows of key dims and stored as half [dk][dv].
+// staged through LDS as rows of key dims and stored as half [dk][dv], each
+// row d divided by its power-of-two scale sigU[d] (row_scale of the row's
+// largest magnitude, taken exactly through LDS).
 // ===========================================================================
 template <int DK, int DV, int C, typename InT>
 __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
@@ -56,6 +60,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
   __shared__ __attribute__((aligned(16))) char sKU[KU_BYTES];
   __shared__ __attribute__((aligned(16))) float sTot[NB][DK];
   __shared__ __attribute__((aligned(16))) float sAft[NB][DK];  // totals of sub-blocks I..NB-1
+  __shared__ unsigned sRowMax[DK];  // largest |U[d][e]| of each row, as float bits
   half_t (*sKh)[HSTR] = reinterpret_cast<half_t (*)[HSTR]>(sKU);
   half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sKU);
 
@@ -77,6 +82,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     load_row<DK, NKS>(gp, row, lk, sc);
   }
   load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV);
+  if (tid < DK) sRowMax[tid] = 0u;
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
     zero_row<NEL>(pad, kf);
     zero_row<NEL>(pad, sc);
@@ -97,7 +103,6 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     float aft = 0.f;
     for (int J = I2; J < NB; ++J) aft += sTot[J][d];
     sAft[I2][d] = aft;
-    if (I2 == 0) Aws[bhn * DK + d] = fexp2(aft);  // a = 2^B
   }
   __syncthreads();
   if (owner) {
@@ -128,18 +133,21 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
         const half4 bb = ld_tr<HSTR, 4>(&sKh[16 * J][16 * D]);
         acc[i] = mfma16x16x16(a, bb, acc[i]);
       }
+      // this lane's four values of row d = 16D + lr
+      const float m = fmaxf(fmaxf(fabsf(acc[i][0]), fabsf(acc[i][1])),
+                            fmaxf(fabsf(acc[i][2]), fabsf(acc[i][3])));
+      atomicMax(&sRowMax[16 * D + lr], __float_as_uint(m));
     }
   }
-  __syncthreads();  // K^ is no longer read
+  __syncthreads();  // K^ is no longer read; the row maxima are complete
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int blk = wave + 4 * i;
     if (blk < NBLK) {
       const int E = blk / ND, D = blk % ND;
-      half4 h;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = (half_t)acc[i][r];
-      *reinterpret_cast<half4*>(&sU[16 * D + lr][16 * E + 4 * lq]) = h;
+      const float inv = inv_scale(row_scale(__uint_as_float(sRowMax[16 * D + lr])));
+      const floatx4 x = acc[i] * inv;
+      *reinterpret_cast<half4*>(&sU[16 * D + lr][16 * E + 4 * lq]) = cvt4(x);
     }
   }
   __syncthreads();
@@ -148,6 +156,9 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     const int d = u / (DV / 8), e8 = (u % (DV / 8)) * 8;
     *reinterpret_cast<half8*>(Ub + d * DV + e8) = *reinterpret_cast<const half8*>(&sU[d][e8]);
   }
+  if (tid < DK)  // (a = 2^B, largest |U| of row d)
+    *reinterpret_cast<float2*>(Aws + 2 * (bhn * DK + tid)) =
+        float2{fexp2(sAft[0][tid]), __uint_as_float(sRowMax[tid])};
 }
 
 // ===========================================================================
@@ -179,27 +190,38 @@ constexpr int kSerialScanLongChain = 256;
 
 // R: chunks per segment kept in registers (2, 4 or 8, the segment length
 // rounded up, so that the clamped loads of a short segment are not repeated)
+//
+// Scales: U_n arrives as half rows divided by row_scale(m_n[d]), m_n[d] its
+// largest magnitude (paired with a_n[d] in one 8-byte load). S_n leaves as
+// half rows divided by row_scale(M_n[d]), with M_n[d] a bound on
+// max_e |S_n[d][e]| that every thread of a row computes identically:
+//   M_0 = max_e |s0[d][e]|,   M_{n+1} = a_n M_n + m_n[d],
+// so the stored rows stay below 2^14 and no row maximum has to be exchanged
+// on the way. The bound composes over segments like (a, U) does. The scales
+// are taken from exponents (v_ldexp) without branches: a branch on freshly
+// loaded data would make the compiler wait for every load in flight.
 template <int kScanRegs>
-__global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict__ Uws,
-                                                        const float* __restrict__ Aws,
-                                                        half_t* __restrict__ Sws,
-                                                        const float* __restrict__ s0,
-                                                        float* __restrict__ sfin, int H, int N,
-                                                        int DK, int DV, int L) {
+__global__ __launch_bounds__(kThreads) void scan_kernel(
+    const half_t* __restrict__ Uws, const float* __restrict__ Aws, half_t* __restrict__ Sws,
+    float* __restrict__ SigS, const float* s0, float* sfin, int H, int N, int DK, int DV, int L) {
+  __shared__ unsigned sM0[8 * (kThreads / kScanSegs) / 32];  // per state row of the block
   const long bh = (long)blockIdx.z * H + blockIdx.y;
   const int seg = threadIdx.x & (kScanSegs - 1);
   const int x8 = 8 * (blockIdx.x * (kThreads / kScanSegs) + (threadIdx.x >> 4));
   const int d = x8 / DV;
   const long DKDV = (long)DK * DV;
   const half_t* U = Uws + bh * N * DKDV + x8;
-  const float* A = Aws + bh * N * DK + d;
+  const float2* A = reinterpret_cast<const float2*>(Aws) + bh * N * DK + d;  // (a, m)
   half_t* S = Sws + bh * N * DKDV + x8;
+  float* SS = SigS + bh * N * DK + d;
+  const bool row_lead = x8 % DV == 0;  // this group stores its row's scale
   const int n0 = min(seg * L, N), n1 = min(n0 + L, N);
 
-  // -- fold this segment into (ag, ug); the chunks of one register block stay cached
-  float ag = 1.f, ug[8];
+  // -- fold this segment into (ag, ug) and its bound mg; the chunks of one
+  // register block stay cached
+  float ag = 1.f, mg = 0.f, ug[8];
   half8 uc[kScanRegs];
-  float ac[kScanRegs];
+  float2 ac[kScanRegs];
 #pragma unroll
   for (int c = 0; c < 8; ++c) ug[c] = 0.f;
   for (int nb = n0; nb < n1; nb += kScanRegs) {
@@ -214,9 +236,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
 #pragma unroll
     for (int i = 0; i < kScanRegs; ++i) {
       if (nb + i < n1) {
+        const float su = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(ac[i].y));
 #pragma unroll
-        for (int c = 0; c < 8; ++c) ug[c] = ac[i] * ug[c] + (float)uc[i][c];
-        ag *= ac[i];
+        for (int c = 0; c < 8; ++c) ug[c] = fmaf((float)uc[i][c], su, ac[i].x * ug[c]);
+        mg = ac[i].x * mg + ac[i].y;
+        ag *= ac[i].x;
       }
     }
   }
@@ -226,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
     const float ap = dpp_row_shr<CTRL>(ag, 1.f);                         \
     _Pragma("unroll") for (int c = 0; c < 8; ++c) ug[c] =                \
         ag * dpp_row_shr<CTRL>(ug[c], 0.f) + ug[c];                      \
+    mg = ag * dpp_row_shr<CTRL>(mg, 0.f) + mg;                           \
     ag *= ap;                                                            \
   }
   GLA_SCAN_STEP(0x111)
@@ -233,9 +258,17 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
   GLA_SCAN_STEP(0x114)
   GLA_SCAN_STEP(0x118)
 #undef GLA_SCAN_STEP
-  float st0[8], s[8];
-  if (s0) {
+  float st0[8], s[8], M0 = 0.f;
+  if (s0) {  // uniform: the initial state and its row maxima (rows span two waves)
+    if (threadIdx.x < 8 * (kThreads / kScanSegs) / 32) sM0[threadIdx.x] = 0u;
     load_f8(s0 + bh * DKDV + x8, st0);
+    float m = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(st0[c]));
+    __syncthreads();
+    atomicMax(&sM0[(8 * (threadIdx.x >> 4)) / DV], __float_as_uint(m));
+    __syncthreads();
+    M0 = __uint_as_float(sM0[(8 * (threadIdx.x >> 4)) / DV]);
   } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) st0[c] = 0.f;
@@ -243,6 +276,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
   const float ae = dpp_row_shr<0x111>(ag, 1.f);
 #pragma unroll
   for (int c = 0; c < 8; ++c) s[c] = ae * st0[c] + dpp_row_shr<0x111>(ug[c], 0.f);
+  float M = ae * M0 + dpp_row_shr<0x111>(mg, 0.f);
   if (sfin && seg == kScanSegs - 1) {
     float f[8];
 #pragma unroll
@@ -264,9 +298,17 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
 #pragma unroll
     for (int i = 0; i < kScanRegs; ++i) {
       if (nb + i < n1) {
-        store8(S + (long)(nb + i) * DKDV, s);
+        const int es = row_scale_exp(M);
+        const float inv = __builtin_amdgcn_ldexpf(1.f, -es);
+        half8 o;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s[c] = ac[i] * s[c] + (float)uc[i][c];
+        for (int c = 0; c < 8; ++c) o[c] = (half_t)(s[c] * inv);
+        *reinterpret_cast<half8*>(S + (long)(nb + i) * DKDV) = o;
+        if (row_lead) SS[(long)(nb + i) * DK] = __builtin_amdgcn_ldexpf(1.f, es);
+        const float su = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(ac[i].y));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = fmaf((float)uc[i][c], su, ac[i].x * s[c]);
+        M = ac[i].x * M + ac[i].y;
       }
     }
   }
@@ -278,31 +320,36 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const half_t* __restrict
 // state (the segmented scan above touches 16 chunks in 64-byte pieces per
 // load and makes two dependent memory round trips per workgroup); with
 // enough chains the loads in flight cover the HBM latency, and each element
-// follows the recurrence S_{n+1} = a_n S_n + U_n exactly in order.
+// follows the recurrence S_{n+1} = a_n S_n + U_n exactly in order. Scales as
+// in scan_kernel; the DV/8 threads of a state row are neighbouring lanes,
+// which take the row maximum of s0 by lane permutations.
 template <int W>
-__global__ __launch_bounds__(kThreads) void scan_serial_kernel(const half_t* __restrict__ Uws,
-                                                               const float* __restrict__ Aws,
-                                                               half_t* __restrict__ Sws,
-                                                               const float* __restrict__ s0,
-                                                               float* __restrict__ sfin, int N,
-                                                               int DK, int DV, long groups) {
+__global__ __launch_bounds__(kThreads) void scan_serial_kernel(
+    const half_t* __restrict__ Uws, const float* __restrict__ Aws, half_t* __restrict__ Sws,
+    float* __restrict__ SigS, const float* s0, float* sfin, int N, int DK, int DV, long groups) {
   const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
+  // groups is a multiple of DV/8, so the lanes of one state row leave together
   if (gid >= groups) return;
   const long DKDV = (long)DK * DV, per = DKDV / 8;
   const long bh = gid / per;
   const int x8 = 8 * (int)(gid - bh * per), d = x8 / DV;
   const half_t* U = Uws + bh * N * DKDV + x8;
-  const float* A = Aws + bh * N * DK + d;
+  const float2* A = reinterpret_cast<const float2*>(Aws) + bh * N * DK + d;  // (a, m)
   half_t* S = Sws + bh * N * DKDV + x8;
-  float s[8];
+  float* SS = SigS + bh * N * DK + d;
+  const bool row_lead = x8 % DV == 0;
+  float s[8], M = 0.f;
   if (s0) {
     load_f8(s0 + bh * DKDV + x8, s);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) M = fmaxf(M, fabsf(s[c]));
+    M = DV == 64 ? group_max<8>(M) : group_max<4>(M);
   } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) s[c] = 0.f;
   }
   half8 u[W];
-  float a[W];
+  float2 a[W];
 #pragma unroll
   for (int i = 0; i < W; ++i) {
     const long m = i < N ? i : N - 1;
@@ -314,9 +361,18 @@ __global__ __launch_bounds__(kThreads) void scan_serial_kernel(const half_t* __r
     for (int i = 0; i < W; ++i) {
       const int n = n0 + i;
       if (n < N) {
-        store8(S + n * DKDV, s);  // the state entering chunk n
+        // the state entering chunk n
+        const int es = row_scale_exp(M);
+        const float inv = __builtin_amdgcn_ldexpf(1.f, -es);
+        half8 o;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s[c] = a[i] * s[c] + (float)u[i][c];
+        for (int c = 0; c < 8; ++c) o[c] = (half_t)(s[c] * inv);
+        *reinterpret_cast<half8*>(S + n * DKDV) = o;
+        if (row_lead) SS[(long)n * DK] = __builtin_amdgcn_ldexpf(1.f, es);
+        const float su = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(a[i].y));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = fmaf((float)u[i][c], su, a[i].x * s[c]);
+        M = a[i].x * M + a[i].y;
       }
       const long m = n + W < N ? n + W : N - 1;  // refill the slot (clamped)
       u[i] = *reinterpret_cast<const half8*>(U + m * DKDV);
@@ -343,7 +399,7 @@ hipError_t summaries_t(const Problem& p, int b0, int nb, const DirPack& dirs, co
                      static_cast<const InT*>(k) + tok * DK, static_cast<const InT*>(v) + tok * DV,
                      static_cast<const InT*>(gk) + tok * DK,
                      reinterpret_cast<half_t*>(ws + w.off_U) + bhn * DK * DV,
-                     reinterpret_cast<float*>(ws + w.off_a) + bhn * DK, p.T, p.H, p.N, p.gh,
+                     reinterpret_cast<float*>(ws + w.off_a) + 2 * bhn * DK, p.T, p.H, p.N, p.gh,
                      p.gw, dirs);
   return hipGetLastError();
 }
@@ -362,9 +418,10 @@ WsLayout workspace_layout(const Problem& p) {
   WsLayout w;
   w.off_U = (size_t)kCtrlWords * sizeof(unsigned);
   w.off_a = w.off_U + up(units * p.dk * p.dv * sizeof(half_t));
-  w.off_S = w.off_a + up(units * p.dk * sizeof(float));
+  w.off_S = w.off_a + up(units * p.dk * 2 * sizeof(float));
   w.off_g = w.off_S + up(units * p.dk * p.dv * sizeof(half_t));
-  w.total = w.off_g + up(units * p.dk * sizeof(float));
+  w.off_ss = w.off_g + up(units * p.dk * 2 * sizeof(float));
+  w.total = w.off_ss + up(units * p.dk * sizeof(float));
   return w;
 }
 
@@ -404,8 +461,9 @@ hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* 
     auto serial = p.N >= 64 ? scan_serial_kernel<16> : scan_serial_kernel<8>;
     hipLaunchKernelGGL(serial, dim3((unsigned)((groups + kThreads - 1) / kThreads)), dim3(kThreads),
                        0, s, reinterpret_cast<const half_t*>(ws + w.off_U) + bhn * dkdv,
-                       reinterpret_cast<const float*>(ws + w.off_a) + bhn * p.dk,
+                       reinterpret_cast<const float*>(ws + w.off_a) + 2 * bhn * p.dk,
                        reinterpret_cast<half_t*>(ws + w.off_S) + bhn * dkdv,
+                       reinterpret_cast<float*>(ws + w.off_ss) + bhn * p.dk,
                        s0 ? s0 + st : nullptr, sfin ? sfin + st : nullptr, p.N, p.dk, p.dv,
                        groups);
     return hipGetLastError();
@@ -413,8 +471,9 @@ hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* 
   auto kernel = L <= 2 ? scan_kernel<2> : L <= 4 ? scan_kernel<4> : scan_kernel<8>;
   hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s,
                      reinterpret_cast<const half_t*>(ws + w.off_U) + bhn * dkdv,
-                     reinterpret_cast<const float*>(ws + w.off_a) + bhn * p.dk,
+                     reinterpret_cast<const float*>(ws + w.off_a) + 2 * bhn * p.dk,
                      reinterpret_cast<half_t*>(ws + w.off_S) + bhn * dkdv,
+                     reinterpret_cast<float*>(ws + w.off_ss) + bhn * p.dk,
                      s0 ? s0 + st : nullptr, sfin ? sfin + st : nullptr, p.H, p.N, p.dk, p.dv,
                      L);
   return hipGetLastError();

@@ -16,10 +16,13 @@ struct Problem {
 };
 
 // Byte offsets of the arrays inside the workspace: the control words (fixed
-// size, offset 0), U, a, S (S also holds the single-pass segment aggregates)
-// and the single-pass segment decays.
+// size, offset 0), U (half rows divided by their scales), the pairs
+// (a_n[d], row scale of U_n row d) as float2 [B][H][N][dk], S (S also holds
+// the single-pass segment aggregates), the single-pass segment pairs
+// (decay, row scale), and the row scales of the three-phase S (float
+// [B][H][N][dk]). Every scale is a power of two.
 struct WsLayout {
-  size_t off_U, off_a, off_S, off_g, total;
+  size_t off_U, off_a, off_S, off_g, off_ss, total;
 };
 
 WsLayout workspace_layout(const Problem& p);

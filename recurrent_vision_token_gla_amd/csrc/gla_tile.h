@@ -132,6 +132,69 @@ __device__ __forceinline__ void store_f8(float* p, const float (&a)[8]) {
   *reinterpret_cast<float4*>(p + 4) = float4{a[4], a[5], a[6], a[7]};
 }
 
+// ---- power-of-two scales that keep half tiles in range ----------------------
+// A state row (summary U, boundary state S, look-back aggregate) is stored in
+// half divided by a power of two sigma >= 1: sigma = 1 while the row's largest
+// magnitude m stays below 2^14, else the power of two that brings m into
+// [2^13, 2^14). So the stored values stay far inside the half range and the
+// row keeps float's upper range. Zero and non-finite m give sigma = 1.
+constexpr float kRowRange = 16384.f;  // 2^14
+__device__ __forceinline__ float row_scale(float m) {
+  const int eb = (int)((__float_as_uint(m) >> 23) & 0xffu);  // m >= 0: biased exponent
+  const int e = eb - 140;  // m < 2^(eb-126), so m / 2^e < 2^14
+  return (e <= 0 || eb == 255) ? 1.f : __uint_as_float((unsigned)(e + 127) << 23);
+}
+// 1 / sigma, exact (sigma is a power of two between 1 and 2^114)
+__device__ __forceinline__ float inv_scale(float sigma) {
+  return __uint_as_float(((254u << 23) - __float_as_uint(sigma)) & 0x7f800000u);
+}
+// The exponent e >= 0 of row_scale(m) = 2^e, without a branch (non-finite m
+// gives a large scale; such rows are non-finite anyway).
+__device__ __forceinline__ int row_scale_exp(float m) {
+  return max((int)((__float_as_uint(m) >> 23) & 0xffu) - 140, 0);
+}
+
+// Eight floats to half with the packed round-to-nearest-even conversion.
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ half8 cvt8(const float (&x)[8]) {
+  const floatx8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, half8);
+}
+__device__ __forceinline__ half4 cvt4(const floatx4& x) { return __builtin_convertvector(x, half4); }
+
+// Largest value over the aligned group of LANES consecutive lanes the caller
+// belongs to (every lane of the group active): DPP lane permutations within
+// a row of 16 (quad swaps, then the half-row mirror), shuffles beyond.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float m) {
+  return fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), CTRL, 0xf,
+                                                              0xf, false)));
+}
+template <int LANES>
+__device__ __forceinline__ float group_max(float m) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64, "");
+  m = dpp_max<0xB1>(m);                       // quad_perm [1,0,3,2]: lane ^ 1
+  m = dpp_max<0x4E>(m);                       // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (LANES >= 8) m = dpp_max<0x141>(m);   // row_half_mirror: the other quad
+  if constexpr (LANES >= 16) m = dpp_max<0x140>(m);  // row_mirror: the other half-row
+  if constexpr (LANES >= 32) m = fmaxf(m, __shfl_xor(m, 16));
+  if constexpr (LANES >= 64) m = fmaxf(m, __shfl_xor(m, 32));
+  return m;
+}
+
+// A (decay, row scale) pair published as one 8-byte device-coherent access.
+__device__ __forceinline__ void st_dev2(float* p, float a, float b) {
+  const unsigned long long v =
+      (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32))};
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_row_shr(float x, float fill) {
   return __int_as_float(

@@ -1,9 +1,9 @@
 // gfx950 kernel of the Spatial SwiGLU channel mixer's fused core.
 //
 // GTR's channel mixer (ai.info summary of GTR, "Methodology in Plain
-// English"; project page, "How GTR Works") inserts a 3x3 depthwise
-// convolution, taken on the 2-D patch grid, into the value branch of a
-// SwiGLU block. With the two input projections already applied by the caller
+// English"; project page, "How GTR Works") is a SwiGLU whose non-gated input
+// path first passes through a per-channel 3x3 spatial filter over the patch
+// grid. With the two input projections already applied by the caller
 // (a = gate branch, u = value branch, both [B][T][F] in raster token order),
 // this kernel computes, per token (y, x) and channel c,
 //   h[y][x][c] = silu(a[y][x][c]) * (bias[c] + sum_{i,j=0..2} w[c][i][j] u[y+i-1][x+j-1][c])

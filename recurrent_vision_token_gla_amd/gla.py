@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 from typing import Optional, Sequence, Union
 
 import torch
@@ -18,13 +19,27 @@ L2R, R2L, T2B, B2T = 0, 1, 2, 3
 F16, F32 = 0, 1
 SCHED_AUTO, SCHED_SINGLE_PASS, SCHED_THREE_PHASE = 0, 1, 2
 CTRL_BYTES = 65536  # control words at the start of every workspace
-OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_UNPREPARED = 0, -1, -2, -3, -4, -5
+ERR_SPIN = 1  # sticky error bit: a single-pass wait ran out of its poll budget
+ABI_VERSION = 5
 
 # every symbol declared in include/gla.h
 EXPORTS = ["gla_abi_version", "gla_fwd_workspace_bytes", "gla_workspace_layout", "gla_fwd",
            "gla_fwd_state", "gla_fwd_gated", "gla_fwd_schedule", "gla_auto_schedule", "gla_workspace_init",
+           "gla_workspace_release", "gla_workspace_is_prepared", "gla_workspace_status",
            "gla_chunk_summaries", "gla_spatial_swiglu", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
            "gla_status_string", "gla_last_error_detail"]
+
+# With check_errors(True), every forward call made through this module waits
+# for its stream and raises if the workspace's sticky error word is set
+# (skipped while the stream is being captured into a graph). Off by default:
+# the check synchronises.
+_check_errors = False
+
+
+def check_errors(on: bool) -> None:
+    global _check_errors
+    _check_errors = bool(on)
 
 _lib = None
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -53,7 +68,7 @@ def load():
     lib.gla_fwd_workspace_bytes.restype = _sz
     lib.gla_fwd_workspace_bytes.argtypes = [_i32] * 7
     lib.gla_workspace_layout.restype = _i32
-    lib.gla_workspace_layout.argtypes = [_i32] * 7 + [ctypes.POINTER(_sz)] * 4
+    lib.gla_workspace_layout.argtypes = [_i32] * 7 + [ctypes.POINTER(_sz)] * 5
     lib.gla_fwd.restype = _i32
     lib.gla_fwd.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
     lib.gla_fwd_state.restype = _i32
@@ -69,6 +84,12 @@ def load():
     lib.gla_auto_schedule.argtypes = [_i32] * 7
     lib.gla_workspace_init.restype = _i32
     lib.gla_workspace_init.argtypes = [_vp, _sz, _vp]
+    lib.gla_workspace_release.restype = _i32
+    lib.gla_workspace_release.argtypes = [_vp]
+    lib.gla_workspace_is_prepared.restype = _i32
+    lib.gla_workspace_is_prepared.argtypes = [_vp]
+    lib.gla_workspace_status.restype = _i32
+    lib.gla_workspace_status.argtypes = [_vp, _sz, ctypes.POINTER(ctypes.c_uint32), _i32, _vp]
     lib.gla_chunk_summaries.restype = _i32
     lib.gla_chunk_summaries.argtypes = [_vp] * 3 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
     lib.gla_state_scan.restype = _i32
@@ -120,18 +141,24 @@ def workspace_bytes(B, H, grid_h, grid_w, dk, dv, chunk=64) -> int:
 
 
 def workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk=64):
-    """(off_U, off_a, off_S, total) byte offsets inside the workspace."""
-    vals = [_sz() for _ in range(4)]
+    """(off_U, off_a, off_S, off_scales, total) byte offsets inside the workspace."""
+    vals = [_sz() for _ in range(5)]
     _check(load().gla_workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk,
                                        *[ctypes.byref(x) for x in vals]), "gla_workspace_layout")
     return tuple(int(x.value) for x in vals)
 
 
-def alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk=64, device=None) -> torch.Tensor:
-    """A workspace for this problem, zero-filled (its control words must start
-    at zero; every call leaves them zero)."""
+def alloc_workspace(B, H, grid_h, grid_w, dk, dv, chunk=64, device=None,
+                    prepare: bool = True) -> torch.Tensor:
+    """A workspace for this problem. With prepare (the default) it is prepared
+    for the single pass by gla_workspace_init, and released from the
+    library's record of prepared workspaces when the tensor is collected."""
     n = workspace_bytes(B, H, grid_h, grid_w, dk, dv, chunk)
-    return torch.zeros(max(n, CTRL_BYTES), dtype=torch.uint8, device=device or "cuda")
+    ws = torch.empty(max(n, CTRL_BYTES), dtype=torch.uint8, device=device or "cuda")
+    if prepare:
+        workspace_init(ws)
+        weakref.finalize(ws, load().gla_workspace_release, ws.data_ptr())
+    return ws
 
 
 def auto_schedule(B, H, grid_h, grid_w, dk, dv, chunk=64) -> int:
@@ -144,16 +171,43 @@ def auto_schedule(B, H, grid_h, grid_w, dk, dv, chunk=64) -> int:
 
 
 def workspace_init(workspace: torch.Tensor, stream=None) -> None:
-    """Zero the control words (and the sticky error word) with a kernel."""
+    """Prepare a workspace for the single pass: zero its control words (and
+    the sticky error word) with a kernel and record it as prepared."""
     ws, nws = _ws(workspace, workspace.device)
     with _on_device(workspace.device):
         st = load().gla_workspace_init(ws, nws, _stream_ptr(stream))
     _check(st, "gla_workspace_init")
 
 
-def workspace_error(workspace: torch.Tensor) -> int:
-    """The sticky error word (bit 0: a single-pass wait ran out). Syncs."""
-    return int(workspace[:4].view(torch.int32).item())
+def workspace_release(workspace: torch.Tensor) -> None:
+    """Drop a workspace from the library's record of prepared workspaces."""
+    _check(load().gla_workspace_release(workspace.data_ptr()), "gla_workspace_release")
+
+
+def is_prepared(workspace: torch.Tensor) -> bool:
+    return bool(load().gla_workspace_is_prepared(workspace.data_ptr()))
+
+
+def workspace_error(workspace: torch.Tensor, clear: bool = False, stream=None) -> int:
+    """The sticky error word (bit 0: a single-pass wait ran out), read after
+    the work queued on the stream; optionally cleared. Synchronises."""
+    ws, nws = _ws(workspace, workspace.device)
+    bits = ctypes.c_uint32(0)
+    with _on_device(workspace.device):
+        st = load().gla_workspace_status(ws, nws, ctypes.byref(bits), int(clear),
+                                         _stream_ptr(stream))
+    _check(st, "gla_workspace_status")
+    return int(bits.value)
+
+
+def _after_call(workspace: torch.Tensor, stream) -> None:
+    """With check_errors on: raise if the call left the sticky error word set
+    (only a prepared workspace runs the single pass and has one)."""
+    if not _check_errors or torch.cuda.is_current_stream_capturing() or not is_prepared(workspace):
+        return
+    bits = workspace_error(workspace, clear=True, stream=stream)
+    if bits:
+        raise GLAError(E_HIP, f"single-pass wait ran out (error bits {bits:#x})")
 
 
 def _ws(workspace: torch.Tensor, device):
@@ -216,6 +270,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
                                 out.data_ptr(), B, H, grid_h, grid_w, dk, dv, _dirs(direction, B),
                                 chunk, _dtype_code(q), ws, nws, _stream_ptr(stream))
         _check(st, "gla_fwd")
+        _after_call(workspace, stream)
         return out
     return fwd_state(q, k, v, gk, grid_h, grid_w, direction, chunk, return_state=False, out=out,
                      workspace=workspace, stream=stream, schedule=schedule)
@@ -256,6 +311,7 @@ def fwd_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tenso
                                      _dirs(direction, B), chunk, _dtype_code(q), p0, pf, schedule,
                                      ws, nws, _stream_ptr(stream))
     _check(st, "gla_fwd_schedule")
+    _after_call(workspace, stream)
     return (out, s_final) if return_state else out
 
 
@@ -288,6 +344,7 @@ def fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tenso
                                   _dirs(direction, B), chunk, _dtype_code(q), p0, pf, ws, nws,
                                   _stream_ptr(stream))
     _check(st, "gla_fwd_gated")
+    _after_call(workspace, stream)
     return out
 
 
@@ -335,14 +392,39 @@ def chunk_outputs(q, k, v, gk, grid_h, grid_w, direction=L2R, chunk=64, workspac
 
 
 def workspace_views(workspace: torch.Tensor, B, H, grid_h, grid_w, dk, dv, chunk=64):
-    """Views of U [B,H,N,dk,dv] f16, a [B,H,N,dk] f32, S [B,H,N,dk,dv] f16."""
-    off_U, off_a, off_S, _ = workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk)
+    """Views of the stored arrays of the three phases: U [B,H,N,dk,dv] f16,
+    a [B,H,N,dk] f32, S [B,H,N,dk,dv] f16, m [B,H,N,dk] f32 (the largest
+    |U| of each row; a and m are the two halves of the stored (a, m) pairs)
+    and the row scales sigS [B,H,N,dk] f32. The value of U row d is
+    U[..., d, :] * row_scale(m[..., d]), that of S row d is
+    S[..., d, :] * sigS[..., d]."""
+    off_U, off_a, off_S, off_ss, _ = workspace_layout(B, H, grid_h, grid_w, dk, dv, chunk)
     N = -(-(grid_h * grid_w) // chunk)
     n_us = B * H * N * dk * dv
+    n_a = B * H * N * dk
     U = workspace[off_U:off_U + 2 * n_us].view(torch.float16).view(B, H, N, dk, dv)
-    a = workspace[off_a:off_a + 4 * B * H * N * dk].view(torch.float32).view(B, H, N, dk)
+    pairs = workspace[off_a:off_a + 8 * n_a].view(torch.float32).view(B, H, N, dk, 2)
     S = workspace[off_S:off_S + 2 * n_us].view(torch.float16).view(B, H, N, dk, dv)
-    return U, a, S
+    sig_s = workspace[off_ss:off_ss + 4 * n_a].view(torch.float32).view(B, H, N, dk)
+    return U, pairs[..., 0], S, pairs[..., 1], sig_s
+
+
+def workspace_states(workspace: torch.Tensor, B, H, grid_h, grid_w, dk, dv, chunk=64):
+    """(U, a, S) as float64 host arrays with the row scales applied."""
+    U, a, S, m, ss = (x.double().cpu().numpy()
+                      for x in workspace_views(workspace, B, H, grid_h, grid_w, dk, dv, chunk))
+    return U * row_scale(m)[..., None], a, S * ss[..., None]
+
+
+def row_scale(m):
+    """The power-of-two scale a state row with largest magnitude m is stored
+    divided by (the library's rule): 1 while m < 2^14, else the power of two
+    that brings m into [2^13, 2^14)."""
+    import numpy as np
+    m = np.asarray(m, np.float32)
+    e = ((m.view(np.uint32) >> 23) & 0xFF).astype(np.int64) - 140
+    out = np.ldexp(np.float32(1), np.maximum(e, 0)).astype(np.float64)
+    return np.where((e <= 0) | (e == 115), 1.0, out)
 
 
 def scan_perm(grid_h: int, grid_w: int, direction: int, device="cuda", stream=None) -> torch.Tensor:

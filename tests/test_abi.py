@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gla_abi_version() == 4
+    assert lib.gla_abi_version() == gla.ABI_VERSION == 5
     for st in (0, -1, -2, -3, -4, 7):
         s = lib.gla_status_string(st)
         assert s and isinstance(s, bytes)
@@ -47,18 +47,21 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # control words (64 KiB) + U (f16) + a (f32) + S (f16) + segment decays (f32),
-    # each padded to 256 bytes
+    # control words (64 KiB) + U (f16) + (a, U row scale) pairs (2 x f32) + S (f16)
+    # + single-pass segment pairs (2 x f32) + S row scales (f32), each padded to
+    # 256 bytes
     B, H, gh, gw, dk, dv, C = 1, 6, 40, 40, 64, 64, 64
     N = 25
     units = B * H * N
-    expect = 65536 + units * dk * dv * 2 + units * dk * 4 + units * dk * dv * 2 + units * dk * 4
+    expect = (65536 + units * dk * dv * 2 + units * dk * 8 + units * dk * dv * 2
+              + units * dk * 8 + units * dk * 4)
     assert gla.workspace_bytes(B, H, gh, gw, dk, dv, C) == expect
     assert gla.workspace_bytes(0, H, gh, gw, dk, dv, C) == 0
     assert gla.workspace_bytes(1, 1, 5, 7, 32, 32, 16) > 0
     assert gla.workspace_bytes(1, 1, 8, 8, 48, 32, 16) == 0  # unsupported dk
-    off_U, off_a, off_S, total = gla.workspace_layout(B, H, gh, gw, dk, dv, C)
+    off_U, off_a, off_S, off_sc, total = gla.workspace_layout(B, H, gh, gw, dk, dv, C)
     assert off_U == 65536 and off_a % 256 == 0 and off_S % 256 == 0 and total == expect
+    assert off_sc % 256 == 0 and off_sc + units * dk * 4 == total
 
 
 FAKE = 0x10000  # 256-aligned, never dereferenced: every call below fails validation first
@@ -153,9 +156,41 @@ def test_schedule_and_workspace_init_validate(lib):
     # 4097 chunks in one chain: more than the single pass waits on
     assert sched(gla.SCHED_SINGLE_PASS, gh=4097, gw=16, chunk=16) == gla.E_UNSUPPORTED
     assert sched(gla.SCHED_SINGLE_PASS, ws_bytes=100) == gla.E_WORKSPACE
+    # a workspace that gla_workspace_init has not prepared: no single pass
+    assert sched(gla.SCHED_SINGLE_PASS) == gla.E_UNPREPARED
+    assert b"gla_workspace_init" in lib.gla_last_error_detail()
     assert lib.gla_workspace_init(None, 1 << 20, None) == gla.E_ARG
     assert lib.gla_workspace_init(FAKE + 0x10, 1 << 20, None) == gla.E_ARG
     assert lib.gla_workspace_init(FAKE, 65535, None) == gla.E_WORKSPACE
+
+
+def test_workspace_record_and_status_validate(lib):
+    assert lib.gla_workspace_is_prepared(FAKE) == 0
+    assert lib.gla_workspace_is_prepared(None) == 0
+    assert lib.gla_workspace_release(None) == gla.E_ARG
+    assert lib.gla_workspace_release(FAKE) == gla.OK  # not recorded: nothing to drop
+    bits = ctypes.c_uint32(7)
+    assert lib.gla_workspace_status(None, 1 << 20, ctypes.byref(bits), 0, None) == gla.E_ARG
+    assert lib.gla_workspace_status(FAKE + 0x10, 1 << 20, ctypes.byref(bits), 0, None) == gla.E_ARG
+    assert lib.gla_workspace_status(FAKE, 1 << 20, None, 0, None) == gla.E_ARG
+    assert lib.gla_workspace_status(FAKE, 100, ctypes.byref(bits), 0, None) == gla.E_WORKSPACE
+    assert bits.value == 7  # untouched by failed calls
+    assert lib.gla_status_string(gla.E_UNPREPARED).startswith(b"GLA_E_UNPREPARED")
+
+
+def test_state_overlap_validates(lib):
+    arr = (ctypes.c_int32 * 1)(0)
+    st = FAKE + 0x10000  # state [1][1][32][32] float = 4 KiB
+
+    def state(s0, sf):
+        return lib.gla_fwd_state(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
+                                 FAKE + 0x4000, 1, 1, 4, 4, 32, 32, arr, 16, 0, s0, sf,
+                                 FAKE + 0x5000, 100, None)
+    # s_final overlapping s0 without being s0 is rejected before the workspace
+    # check; s_final == s0 passes it (and fails on the tiny workspace)
+    assert state(st, st + 16) == gla.E_ARG
+    assert state(st, st) == gla.E_WORKSPACE
+    assert state(st, st + 4096) == gla.E_WORKSPACE
 
 
 def test_auto_schedule(lib):

@@ -57,6 +57,8 @@ def test_workspace_of_any_dtype_is_sized_in_bytes(inputs):
     ref = gla.fwd(q, k, v, g, 9, 17, [0, 1], 16)
     n = gla.workspace_bytes(2, 2, 9, 17, 32, 64, 16)
     ws32 = torch.zeros((n + 3) // 4, dtype=torch.float32, device="cuda")
+    gla.workspace_init(ws32)  # prepared like the binding's own: same schedule, same bits
     o = gla.fwd(q, k, v, g, 9, 17, [0, 1], 16, workspace=ws32)
     torch.cuda.synchronize()
     assert torch.equal(o, ref)
+    gla.workspace_release(ws32)

@@ -101,7 +101,7 @@ def test_phase_intermediates_match_chunked_model():
     ws = gla.chunk_summaries(tk, tv, tg, gh, gw, dirs, C)
     gla.state_scan(B, H, gh, gw, dk, dv, C, ws)
     torch.cuda.synchronize()
-    U, a, S = (x.double().cpu().numpy() for x in gla.workspace_views(ws, B, H, gh, gw, dk, dv, C))
+    U, a, S = gla.workspace_states(ws, B, H, gh, gw, dk, dv, C)
     s = lambda x: oracle.to_scan(x, gh, gw, dirs)
     _, U_ref, a_ref, S_ref, _ = oracle.chunkwise(s(q), s(k), s(v), s(g), C, return_states=True)
     say(f"U err {rel_err(U, U_ref):.2e}  a err {rel_err(a, a_ref):.2e}  "

@@ -124,7 +124,7 @@ def test_scan_phase_with_state_matches_chunked_model():
     ws = gla.chunk_summaries(tk, tv, tg, gh, gw, dirs, C)
     gla.state_scan(B, H, gh, gw, dk, dv, C, ws, s0=ts0, s_final=sf)
     torch.cuda.synchronize()
-    _, _, S = (x.double().cpu().numpy() for x in gla.workspace_views(ws, B, H, gh, gw, dk, dv, C))
+    _, _, S = gla.workspace_states(ws, B, H, gh, gw, dk, dv, C)
     s = lambda x: oracle.to_scan(x, gh, gw, dirs)
     _, _, _, S_ref, sT_ref = oracle.chunkwise(s(q), s(k), s(v), s(g), C, return_states=True, s0=s0)
     assert rel_err(S, S_ref) <= 2e-3
@@ -156,7 +156,7 @@ def test_serial_scan_with_carried_state(B, H, gh, gw, dk, dv, chunk):
     ws = gla.chunk_summaries(tk, tv, tg, gh, gw, dirs, chunk)
     gla.state_scan(B, H, gh, gw, dk, dv, chunk, ws, s0=ts0)
     torch.cuda.synchronize()
-    _, _, S = (x.double().cpu().numpy() for x in gla.workspace_views(ws, B, H, gh, gw, dk, dv, chunk))
+    _, _, S = gla.workspace_states(ws, B, H, gh, gw, dk, dv, chunk)
     s = lambda x: oracle.to_scan(x, gh, gw, dirs)
     _, _, _, S_ref, _ = oracle.chunkwise(s(q), s(k), s(v), s(g), chunk, return_states=True, s0=s0)
     assert rel_err(S, S_ref) <= 2e-3
