@@ -206,6 +206,23 @@ int gla_fwd_gated(const void* q, const void* k, const void* v, const void* gk,
                   float* s_final, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): gla_fwd without a
+ * workspace argument. The workspace is a static device array of 64 MiB
+ * inside the library, one per GPU, held until the process ends; the call
+ * allocates nothing (no hipMalloc, no library allocation). Problems whose
+ * gla_fwd_workspace_bytes exceed 64 MiB return GLA_E_WORKSPACE (with the
+ * sizes in gla_last_error_detail). The first call on a GPU also enqueues one
+ * small kernel on `stream` that zeroes the array's control words. Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (concurrent streams or threads) race and give wrong results; serialise
+ * them. Otherwise the same as gla_fwd (GTR project page, "A Kernel That
+ * Makes Recurrence Fast"). */
+int gla_fwd_noalloc(const void* q, const void* k, const void* v, const void* gk,
+                    void* o, int B, int H, int grid_h, int grid_w, int dk,
+                    int dv, const int32_t* dir, int chunk, int dtype,
+                    void* stream);
+
 /* gla_fwd_state with an explicit schedule: GLA_SCHED_AUTO (what gla_fwd and
  * gla_fwd_state do), GLA_SCHED_SINGLE_PASS or GLA_SCHED_THREE_PHASE. The
  * single pass returns GLA_E_UNPREPARED on a workspace gla_workspace_init has

@@ -205,9 +205,72 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
                       workspace_bytes, epi, stream);
 }
 
+// ---- allocation-free forward ----------------------------------------------
+// gla_fwd_noalloc takes its workspace from this file-scope device array, one
+// copy per GPU the library runs on (kept until the process ends). Host code
+// never passes the array's name to a kernel: the per-device address from
+// hipGetSymbolAddress is kept below and used instead.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// The calling thread's current device's copy of `scratch`: on its first use on
+// a device, the address is looked up, the control words are zeroed by a kernel
+// on `stream` (ordered before the call that needs them) and the address is
+// recorded as a prepared workspace. Returns GLA_OK or GLA_E_HIP/_UNSUPPORTED.
+int scratch_for_device(hipStream_t stream, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return GLA_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    e = gla::launch_ctrl_clear(static_cast<char*>(ptr), stream);
+    if (e != hipSuccess) return fail_hip(e, "scratch control-word clear");
+    {
+      std::lock_guard<std::mutex> lk2(g_prepared_mu);
+      g_prepared[reinterpret_cast<uintptr_t>(ptr)] = kScratchBytes;
+    }
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gla_fwd_noalloc(const void* q, const void* k, const void* v, const void* gk, void* o, int B,
+                    int H, int grid_h, int grid_w, int dk, int dv, const int32_t* dir, int chunk,
+                    int dtype, void* stream) {
+  gla::Problem p;
+  bool empty;
+  GLA_TRY(make_problem(B, H, grid_h, grid_w, dk, dv, chunk, dtype, &p, &empty));
+  if (empty) return GLA_OK;
+  const size_t need = gla::workspace_layout(p).total;
+  if (need > kScratchBytes) {
+    snprintf(g_detail, sizeof(g_detail),
+             "this problem needs %zu bytes of workspace; the allocation-free forward's "
+             "static scratch holds %zu (use gla_fwd with a caller workspace)",
+             need, kScratchBytes);
+    return GLA_E_WORKSPACE;
+  }
+  char* ws = nullptr;
+  GLA_TRY(scratch_for_device(static_cast<hipStream_t>(stream), &ws));
+  return fwd_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, nullptr,
+                  nullptr, ws, kScratchBytes, stream, 0);
+}
 
 int gla_abi_version(void) { return 5; }
 
@@ -415,7 +478,7 @@ const char* gla_status_string(int status) {
     case GLA_OK: return "GLA_OK";
     case GLA_E_ARG: return "GLA_E_ARG: invalid argument (null/misaligned pointer, negative size, bad code, aliasing)";
     case GLA_E_UNSUPPORTED: return "GLA_E_UNSUPPORTED: dk, dv or chunk outside the supported set, or problem too large";
-    case GLA_E_WORKSPACE: return "GLA_E_WORKSPACE: workspace smaller than gla_fwd_workspace_bytes()";
+    case GLA_E_WORKSPACE: return "GLA_E_WORKSPACE: workspace smaller than gla_fwd_workspace_bytes() (see gla_last_error_detail)";
     case GLA_E_HIP: return "GLA_E_HIP: a HIP launch failed (see gla_last_error_detail)";
     case GLA_E_UNPREPARED: return "GLA_E_UNPREPARED: the single pass needs a workspace prepared by gla_workspace_init";
     default: return "unknown GLA status";

@@ -28,7 +28,7 @@ EXPORTS = ["gla_abi_version", "gla_fwd_workspace_bytes", "gla_workspace_layout",
            "gla_fwd_state", "gla_fwd_gated", "gla_fwd_schedule", "gla_auto_schedule", "gla_workspace_init",
            "gla_workspace_release", "gla_workspace_is_prepared", "gla_workspace_status",
            "gla_chunk_summaries", "gla_spatial_swiglu", "gla_state_scan", "gla_chunk_outputs", "gla_scan_perm",
-           "gla_status_string", "gla_last_error_detail"]
+           "gla_status_string", "gla_last_error_detail", "gla_fwd_noalloc"]
 
 # With check_errors(True), every forward call made through this module waits
 # for its stream and raises if the workspace's sticky error word is set
@@ -71,6 +71,8 @@ def load():
     lib.gla_workspace_layout.argtypes = [_i32] * 7 + [ctypes.POINTER(_sz)] * 5
     lib.gla_fwd.restype = _i32
     lib.gla_fwd.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _sz, _vp]
+    lib.gla_fwd_noalloc.restype = _i32
+    lib.gla_fwd_noalloc.argtypes = [_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp]
     lib.gla_fwd_state.restype = _i32
     lib.gla_fwd_state.argtypes = ([_vp] * 5 + [_i32] * 6 + [_i32p, _i32, _i32, _vp, _vp, _vp, _sz,
                                                             _vp])
@@ -274,6 +276,22 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
         return out
     return fwd_state(q, k, v, gk, grid_h, grid_w, direction, chunk, return_state=False, out=out,
                      workspace=workspace, stream=stream, schedule=schedule)
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
+                grid_h: int, grid_w: int, direction: Union[int, Sequence[int]] = L2R,
+                chunk: int = 64, out: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The forward on the library's static scratch (gla_fwd_noalloc): no
+    workspace is allocated; calls on one GPU must not overlap in time."""
+    B, T, H, dk, dv = _shapes(q, k, v, gk, grid_h, grid_w)
+    out = _out(out, (B, T, H, dv), q.dtype, q.device)
+    with _on_device(q.device):
+        st = load().gla_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                                    out.data_ptr(), B, H, grid_h, grid_w, dk, dv,
+                                    _dirs(direction, B), chunk, _dtype_code(q), _stream_ptr(stream))
+    _check(st, "gla_fwd_noalloc")
+    return out
 
 
 def _state_ptr(t: Optional[torch.Tensor], B, H, dk, dv, name, device=None) -> Optional[int]:
