@@ -101,7 +101,12 @@ extern "C" {
 
 enum { GLA_L2R = 0, GLA_R2L = 1, GLA_T2B = 2, GLA_B2T = 3 };
 enum { GLA_F16 = 0, GLA_F32 = 1 };
-enum { GLA_SCHED_AUTO = 0, GLA_SCHED_SINGLE_PASS = 1, GLA_SCHED_THREE_PHASE = 2 };
+enum {
+  GLA_SCHED_AUTO = 0,
+  GLA_SCHED_SINGLE_PASS = 1,  /* one workgroup per chunk, segmented look-back */
+  GLA_SCHED_THREE_PHASE = 2,  /* summaries, boundary scan, outputs */
+  GLA_SCHED_RUNS = 3          /* one workgroup per run of 4 chunks, decoupled look-back */
+};
 enum {
   GLA_OK = 0,
   GLA_E_ARG = -1,          /* null/misaligned pointer, negative size, bad code */

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgla_mi355x.so")
-SOURCES = ["gla_kernels.hip", "gla_gated.hip", "ssw_kernels.hip", "gla_api.hip"]
+SOURCES = ["gla_kernels.hip", "gla_gated.hip", "gla_runs.hip", "ssw_kernels.hip", "gla_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

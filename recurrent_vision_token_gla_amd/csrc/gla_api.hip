@@ -177,6 +177,23 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
   // phases, whose scan reads each element of s0 before it writes the same
   // element of s_final.
   const bool prepared = is_prepared(workspace);
+  if (mode == GLA_SCHED_RUNS) {  // runs of chunks with a decoupled look-back
+    const int nb_max = B < gla::kMaxBatchPerLaunch ? B : gla::kMaxBatchPerLaunch;
+    if (in_place || epi.gate || !gla::runs_fit(p, nb_max)) return GLA_E_UNSUPPORTED;
+    if (!prepared) {
+      snprintf(g_detail, sizeof(g_detail),
+               "the single pass needs a workspace prepared by gla_workspace_init");
+      return GLA_E_UNPREPARED;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
+      const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
+      const hipError_t e = gla::launch_runs(p, b0, nb, pack_dirs(dir, b0, nb), q, k, v, gk, o,
+                                            static_cast<char*>(workspace), s0, s_final, s);
+      if (e != hipSuccess) return fail_hip(e, "runs launch");
+    }
+    return GLA_OK;
+  }
   bool onepass = single_pass_fits(p) && !in_place;
   if (mode == 1 && !onepass) return GLA_E_UNSUPPORTED;
   if (mode == 1 && !prepared) {
@@ -371,7 +388,7 @@ int gla_fwd_schedule(const void* q, const void* k, const void* v, const void* gk
                      int chunk, int dtype, const float* s0, float* s_final, int schedule,
                      void* workspace, size_t workspace_bytes, void* stream) {
   if (schedule != GLA_SCHED_AUTO && schedule != GLA_SCHED_SINGLE_PASS &&
-      schedule != GLA_SCHED_THREE_PHASE)
+      schedule != GLA_SCHED_THREE_PHASE && schedule != GLA_SCHED_RUNS)
     return GLA_E_ARG;
   return fwd_impl(q, k, v, gk, o, B, H, grid_h, grid_w, dk, dv, dir, chunk, dtype, s0, s_final,
                   workspace, workspace_bytes, stream, schedule);

@@ -57,7 +57,7 @@ namespace tile {
 //   3. adds the readout Q^ S_n and stores the outputs.
 // ===========================================================================
 template <int DK, int DV, int C, typename InT, bool kFused, bool kGate>
-__global__ __launch_bounds__(kThreads, kFused ? 3 : 4) void chunk_kernel(
+__global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     const InT* __restrict__ qp, const InT* __restrict__ kp, const InT* __restrict__ vp,
     const InT* __restrict__ gp, InT* __restrict__ op, half_t* __restrict__ Uws,
     float* __restrict__ Aws, half_t* __restrict__ Sws, const float* __restrict__ SigS,
@@ -103,7 +103,6 @@ __global__ __launch_bounds__(kThreads, kFused ? 3 : 4) void chunk_kernel(
   __shared__ float sSigMax;
   __shared__ unsigned sRowMax[kFused ? DK : 1];  // single pass: row maxima of U_n
   __shared__ float sSigU[kFused ? DK : 1];       // single pass: row scales of U_n
-  __shared__ unsigned sSMax;                     // single pass: largest row scale of S_n
   __shared__ unsigned sDone, sPub;
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
@@ -141,7 +140,7 @@ __global__ __launch_bounds__(kThreads, kFused ? 3 : 4) void chunk_kernel(
   // the row table (for the scatter) and the flags below are first read after
   // the barrier that follows the cumulative sums
   chunk_rows<C>(sRow, n * C, T, gh, gw, dir);
-  if (tid == 0) sPub = 0u, sSMax = 0u;
+  if (tid == 0) sPub = 0u;
   if (kFused && tid < DK) sRowMax[tid] = 0u;
 
   // -- this wave's token rows of q, k, gk in the operand layout (waves past
@@ -633,10 +632,7 @@ __global__ __launch_bounds__(kThreads, kFused ? 3 : 4) void chunk_kernel(
 #pragma unroll
         for (int c = 0; c < 8; ++c) o[c] = xs[g][c] * inv;
         *reinterpret_cast<half8*>(&sS[d][x8 % DV]) = cvt8(o);
-        if (x8 % DV == 0) {
-          sSig[d] = sg;
-          atomicMax(&sSMax, __float_as_uint(sg));
-        }
+        if (x8 % DV == 0) sSig[d] = sg;
       }
     }
     __syncthreads();  // S_n complete in LDS; every read of published data done
@@ -644,7 +640,8 @@ __global__ __launch_bounds__(kThreads, kFused ? 3 : 4) void chunk_kernel(
     // row scales of S_n folded into Q^ (factors sigS[d] / max sigS <= 1) and
     // the accumulators taken / max sigS meanwhile
     if (owner) {
-      const float smax = __uint_as_float(sSMax);
+      // the largest row scale, by a reduction within the wave
+      const float smax = group_max<64>(sSig[lane % DK]);
       if (smax != 1.f) {
         const float is = inv_scale(smax);
 #pragma unroll

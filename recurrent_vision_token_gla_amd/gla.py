@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgla_mi35
 
 L2R, R2L, T2B, B2T = 0, 1, 2, 3
 F16, F32 = 0, 1
-SCHED_AUTO, SCHED_SINGLE_PASS, SCHED_THREE_PHASE = 0, 1, 2
+SCHED_AUTO, SCHED_SINGLE_PASS, SCHED_THREE_PHASE, SCHED_RUNS = 0, 1, 2, 3
 CTRL_BYTES = 65536  # control words at the start of every workspace
 OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_UNPREPARED = 0, -1, -2, -3, -4, -5
 ERR_SPIN = 1  # sticky error bit: a single-pass wait ran out of its poll budget

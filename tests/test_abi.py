@@ -151,8 +151,11 @@ def test_schedule_and_workspace_init_validate(lib):
         return lib.gla_fwd_schedule(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
                                     FAKE + 0x4000, 1, 1, gh, gw, 32, 32, arr, chunk, 0, None, None,
                                     schedule, FAKE + 0x5000, ws_bytes, None)
-    assert sched(3) == gla.E_ARG
+    assert sched(4) == gla.E_ARG
     assert sched(-1) == gla.E_ARG
+    # runs of chunks: 64-token chunks only
+    assert sched(gla.SCHED_RUNS, chunk=16) == gla.E_UNSUPPORTED
+    assert sched(gla.SCHED_RUNS, gh=8, gw=8, chunk=64) == gla.E_UNPREPARED
     # 4097 chunks in one chain: more than the single pass waits on
     assert sched(gla.SCHED_SINGLE_PASS, gh=4097, gw=16, chunk=16) == gla.E_UNSUPPORTED
     assert sched(gla.SCHED_SINGLE_PASS, ws_bytes=100) == gla.E_WORKSPACE
