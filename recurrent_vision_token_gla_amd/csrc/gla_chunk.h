@@ -73,19 +73,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   constexpr int SSTR = DV + 16;  // halves, rows of S (read transposed)
   constexpr int USTR = DV + 8;   // halves, rows of the U staging tile
   constexpr int OSTR = DV + 8;   // rows of the output staging tile
-  // the single pass's plain half output is staged column-major (rows = value
-  // columns, 8-byte stores from the accumulators) and read back as token rows
-  // through the transposing LDS read: fewer LDS operations on its critical
-  // path. Each store then covers half a token row, which costs the
-  // throughput-bound three-phase kernel more than it saves; it, the gated
-  // and the fp32 outputs keep token rows.
-  constexpr bool kColO = kFused && !kGate && sizeof(InT) == 2;
-  constexpr int OTSTR = C + 16;  // halves, rows of the column-major output tile
   constexpr int NGR = (DKDV / 8 + kThreads - 1) / kThreads;  // state groups of 8 per thread
   constexpr int LB = 4;  // predecessors per batch of look-back loads
   constexpr float kHalfRange = 8.f, kF32Range = 120.f;  // log2 decay per sub-block
   // K~ is dead once the score blocks are built; the output tile reuses it
-  constexpr int KO0 = C * KSTR * 2, KO1 = kColO ? DV * OTSTR * 2 : C * OSTR * (int)sizeof(InT);
+  constexpr int KO0 = C * KSTR * 2, KO1 = C * OSTR * (int)sizeof(InT);
   constexpr int KO_BYTES = KO0 > KO1 ? KO0 : KO1;
   // one region in turn holds K^, the U staging tile and S (only S unfused)
   constexpr int X0 = DK * SSTR * 2, X1 = kFused ? C * HSTR * 2 : 0, X2 = kFused ? DK * USTR * 2 : 0;
@@ -106,19 +98,16 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __shared__ unsigned sDone, sPub;
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
-  half_t (*sOT)[OTSTR] = reinterpret_cast<half_t (*)[OTSTR]>(sKO);
-  // output block (sub-block I, value block E) of this lane: rows 16I + 4lq + r,
-  // column 16E + lr
+  // The outputs are produced transposed (O^T = V^T A^T + S^T Q^T: the same
+  // operand registers with the two operands swapped), so that each lane holds
+  // four consecutive value columns 16E + 4lq + r of its token 16I + lr and
+  // stages them with one 8-byte (16-byte for float) LDS write into token rows.
   auto stage_out = [&](const floatx4& acc, int E) {
     const int I = threadIdx.x >> 6, lq = (threadIdx.x >> 4) & 3, lr = threadIdx.x & 15;
-    if constexpr (kColO) {
-      half4 hv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hv[r] = (half_t)acc[r];
-      *reinterpret_cast<half4*>(&sOT[16 * E + lr][16 * I + 4 * lq]) = hv;
+    if constexpr (sizeof(InT) == 2) {
+      *reinterpret_cast<half4*>(&sO[16 * I + lr][16 * E + 4 * lq]) = cvt4(acc);
     } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (InT)acc[r];
+      *reinterpret_cast<floatx4*>(&sO[16 * I + lr][16 * E + 4 * lq]) = acc;
     }
   };
   half_t (*sS)[SSTR] = reinterpret_cast<half_t (*)[SSTR]>(sX);
@@ -251,9 +240,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       float tt[8], ff[8];
       lds8(&sTot[I][32 * ks + lk], tt);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        rng = fmaxf(rng, -tt[c]);
-        big = fmaxf(big, fmaxf(fabsf(qf[8 * ks + c]), fabsf(kf[8 * ks + c])));
+      for (int c = 0; c < 8; c += 2) {
+        rng = max3f(rng, -tt[c], -tt[c + 1]);
+        big = max3f(big, fabsf(qf[8 * ks + c]), fabsf(kf[8 * ks + c]));
+        big = max3f(big, fabsf(qf[8 * ks + c + 1]), fabsf(kf[8 * ks + c + 1]));
       }
       if constexpr (kFused) lds8(&sF[I][32 * ks + lk], ff);
       half8 k8, kh8;
@@ -413,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(Af[J][r]));
     if (__any(am > kRowRange)) {
-      sigA = row_scale(group_max<64>(am));
+      sigA = uniform(row_scale(group_max<64>(am)));
       const float inv = inv_scale(sigA);
 #pragma unroll
       for (int J = 0; J < NB; ++J) Af[J] *= inv;
@@ -435,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     // -- O_I = sum_{J<=I} A_IJ V_J + Q^_I S, with A stored / sigA and the
     // readout taken / max sigS
     if (owner) {
-      const float smax = sSigMax;
+      const float smax = uniform(sSigMax);
       const bool rescale = sigA != 1.f || smax != 1.f;
       const float f1 = sigA * inv_scale(smax);
 #pragma unroll
@@ -447,7 +437,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         for (int J = 0; J < NB; ++J) {
           if (J <= I) {
             const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
-            acc = mfma16x16x16(A[J], vb, acc);
+            acc = mfma16x16x16(vb, A[J], acc);
           }
         }
         if (rescale) acc *= f1;
@@ -458,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             const half4 sb = ld_tr<SSTR, 8>(&sS[32 * ks + 4 * hh][16 * E]);
             const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
                                 : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
-            acc = mfma16x16x16(qa, sb, acc);
+            acc = mfma16x16x16(sb, qa, acc);
           }
         }
         if (rescale) acc *= smax;
@@ -545,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
         for (int J = 0; J < NB; ++J) {
           if (J <= I) {
             const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
-            oacc[E] = mfma16x16x16(A[J], vb, oacc[E]);
+            oacc[E] = mfma16x16x16(vb, A[J], oacc[E]);
           }
         }
       }
@@ -641,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     // the accumulators taken / max sigS meanwhile
     if (owner) {
       // the largest row scale, by a reduction within the wave
-      const float smax = group_max<64>(sSig[lane % DK]);
+      const float smax = uniform(group_max<64>(sSig[lane % DK]));
       if (smax != 1.f) {
         const float is = inv_scale(smax);
 #pragma unroll
@@ -665,7 +655,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
             const half4 sb = ld_tr<SSTR, 8>(&sS[32 * ks + 4 * hh][16 * E]);
             const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
                                 : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
-            oacc[E] = mfma16x16x16(qa, sb, oacc[E]);
+            oacc[E] = mfma16x16x16(sb, qa, oacc[E]);
           }
         }
         if (smax != 1.f) oacc[E] *= smax;
@@ -679,20 +669,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // each row of dv values becomes o / sqrt(mean(o^2) + eps) * w * silu(z)
   // (its dv/8 lanes are neighbours and reduce the sum of squares by shuffles)
   constexpr int LPR = DV / 8;  // lanes per output row
-  if constexpr (kColO) {
-    // unit (token block tb, value half eh): lane (lr, lq) takes token
-    // 16tb + lr, values 32eh + 8lq + 0..7, in two transposing reads
-    constexpr int NTB = C / 16, NU = NTB * (DV / 32);
-    for (int u = wave; u < NU; u += kThreads / 64) {
-      const int tb = u % NTB, eh = u / NTB, t = 16 * tb + lr;
-      const half4 lo = ld_tr<OTSTR, 8>(&sOT[32 * eh][16 * tb]);
-      const half4 hi = ld_tr<OTSTR, 8>(&sOT[32 * eh + 4][16 * tb]);
-      if (sRow[t] >= 0)
-        *reinterpret_cast<half8*>(op + (((long)b * T + sRow[t]) * H + h) * DV + 32 * eh + 8 * lq) =
-            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  }
-  for (int u = tid; u < (kColO ? 0 : C * LPR); u += kThreads) {
+  for (int u = tid; u < C * LPR; u += kThreads) {
     const int r = u / LPR, c8 = (u % LPR) * 8;
     const long orow = ((long)b * T + (sRow[r] >= 0 ? sRow[r] : 0)) * H + h;
     if constexpr (!kGate) {

@@ -7,20 +7,24 @@
 // One workgroup takes G consecutive chunks (a run) of one (batch, head)
 // chain. Workgroups are numbered run-major (every chain's run 0, then every
 // chain's run 1, ...), so a run's predecessors were dispatched earlier and
-// have usually finished by the time it needs them. For each of its chunks
-// in order, the workgroup:
-//   - computes the chunk's decay factors, score tile and summary U_n as the
-//     three-phase kernels do;
-//   - keeps the state built inside the run so far, X (zero at the run's
-//     start), in matrix-core accumulators: X <- diag(a_n) X + U_n;
-//   - computes the chunk's outputs as far as the run itself determines them,
-//     O_n = A V + Q^ X_n, and holds O_n in registers with the operand
-//     Q^' = Q^ * 2^(W_n) (W_n: log2 decay from the run's start to the chunk),
-//     the factor the state entering the run still has to be read out with.
-// Then it publishes the run's aggregate (X and the run's decay), takes the
-// state entering the run, S_in, from its predecessors, publishes the
-// inclusive state A_run S_in + X, and finishes every held chunk with
-// O_n += Q^'_n S_in before storing it.
+// have usually finished by the time it needs them. A workgroup walks its run
+// twice:
+//   pass A: each chunk's summary only (k, gk, v: decays, K^ = k 2^(B - b),
+//           U = K^T V on the matrix cores), folded into the run's aggregate
+//           X <- diag(a_n) X + U_n in matrix-core accumulators, and the run's
+//           decay; it publishes the aggregate, takes the state entering the
+//           run, S_in, from its predecessors, and publishes the inclusive
+//           state A_run S_in + X;
+//   pass B: each chunk in full with the state carried along the run in
+//           float accumulators, S <- diag(a_n) S + U_n: scores, A V, the
+//           readout Q^ S and the stores, as the three-phase output kernel
+//           does with S from the boundary scan.
+// So the state never leaves the workgroup inside a run, one launch replaces
+// three, and per chunk HBM sees the forward's own bytes plus a quarter of the
+// run's published and looked-back tiles (pass B's second read of k, gk, v
+// follows pass A's by a few microseconds). The next chunk's inputs load
+// while the current one is processed, pass B's first chunk's during the
+// look-back.
 //
 // Look-back (Merrill and Garland's decoupled look-back, with 8 KB state
 // tiles): every run has a status word, 1 once its aggregate is published, 2
@@ -41,8 +45,6 @@
 // atomics after s_waitcnt on the stores. Each chain counts the runs that have
 // finished reading; the last one clears the chain's words, so they are zero
 // between calls.
-#include <type_traits>
-
 #include "gla_launch.h"
 #include "gla_tile.h"
 
@@ -102,27 +104,34 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
   constexpr int KSTR = DK + 8;   // halves, rows of K~ (read along key dims)
   constexpr int VSTR = DV + 16;  // halves, rows of V (read transposed)
   constexpr int HSTR = DK + 16;  // halves, rows of K^ (read transposed)
-  constexpr int SSTR = DV + 16;  // halves, rows of X / S (read transposed)
+  constexpr int SSTR = DV + 16;  // halves, rows of the aggregate / S (read transposed)
   constexpr int OSTR = DV + 8;   // rows of the output staging tile
   constexpr int NBLK = NE * ND, BPW = (NBLK + 3) / 4;  // U blocks per wave
   constexpr int NGR = (DKDV / 8 + kThreads - 1) / kThreads;  // state groups of 8 per thread
   constexpr int LB = 4;  // look-back tiles per batch of loads
   constexpr float kHalfRange = 8.f, kF32Range = 120.f;
+  constexpr bool kPrefetch = true;
   constexpr int KO0 = C * KSTR * 2, KO1 = C * OSTR * (int)sizeof(InT);
+  // K^ (C x HSTR halves) and the aggregate / S tile (DK x SSTR halves) share
+  // one region, which also carries S_in in float when it changes layout
+  constexpr int KH_BYTES = C * HSTR * 2, XS_BYTES = DK * SSTR * 2;
+  constexpr int BIG0 = KH_BYTES + XS_BYTES, BIG1 = DKDV * 4;
   __shared__ __attribute__((aligned(16))) char sKO[KO0 > KO1 ? KO0 : KO1];  // K~, then outputs
   __shared__ __attribute__((aligned(16))) half_t sV[C][VSTR];
-  __shared__ __attribute__((aligned(16))) half_t sKh[C][HSTR];
-  __shared__ __attribute__((aligned(16))) half_t sXs[DK][SSTR];  // X_n / aggregate / S_in
+  __shared__ __attribute__((aligned(16))) char sBig[BIG0 > BIG1 ? BIG0 : BIG1];
   __shared__ __attribute__((aligned(16))) float sTot[NB][DK], sS7[NB][DK];
-  __shared__ __attribute__((aligned(16))) float sEb[NB][DK], sEw[NB][DK];
+  __shared__ __attribute__((aligned(16))) float sEb[NB][DK], sF[NB][DK];
   __shared__ __attribute__((aligned(16))) float sR1[NB][DK], sR2[NB][DK];
-  __shared__ __attribute__((aligned(16))) float sM[NPAIR][DK], sF[NB][DK];
-  __shared__ __attribute__((aligned(16))) float sWl[DK], sAn[DK], sBt[DK], sSig[DK];
+  __shared__ __attribute__((aligned(16))) float sM[NPAIR][DK];
+  __shared__ __attribute__((aligned(16))) float sWl[DK], sAn[DK], sSig[DK];
   __shared__ unsigned sRowMax[DK];
   __shared__ int sLook[2];
   __shared__ unsigned sPub, sDone;
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
+  half_t (*sKh)[HSTR] = reinterpret_cast<half_t (*)[HSTR]>(sBig);
+  half_t (*sXs)[SSTR] = reinterpret_cast<half_t (*)[SSTR]>(sBig + KH_BYTES);
+  float (*sS32)[DV] = reinterpret_cast<float (*)[DV]>(sBig);
 
   const int run = blockIdx.x / nch, ch = blockIdx.x - run * nch;
   const int h = ch % H, b = ch / H;
@@ -136,45 +145,20 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
   // this lane's state row in the accumulator layout: d = 16 * (wave % ND) + lr
   const int drow = 16 * (wave % ND) + lr;
 
-  floatx4 X[BPW];       // the state built inside the run (rows drow)
-  // The run's chunks are processed by one copy of the chunk code (a loop, so
-  // the kernel fits the instruction cache); their held outputs and operands
-  // pass through a register FIFO: slot G-1 takes the newest chunk and every
-  // step shifts the slots down by one, all with constant indices.
-  // held outputs so far (this wave's 16 tokens): half with the outputs' own
-  // rounding when kHoldHalf (the partial sums are of the outputs' size)
-  constexpr bool kHoldHalf = true;
-  typedef typename std::conditional<kHoldHalf, half4, floatx4>::type HoldT;
-  HoldT Oh[G][NE];
-  half8 Qh[G][NKS];     // held Q^' = Q^ 2^(W_n)
-  auto shift = [&]() {
-#pragma unroll
-    for (int j = 0; j + 1 < G; ++j) {
-#pragma unroll
-      for (int E = 0; E < NE; ++E) Oh[j][E] = Oh[j + 1][E];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) Qh[j][ks] = Qh[j + 1][ks];
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) X[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (tid < DK) sWl[tid] = 0.f;
-  if (tid == 0) sPub = 0u;
-
-  // -- the inputs of the chunk after the current one are loaded while the
-  // current one is processed: this wave's token rows of q, k, gk in the
-  // operand layout and this thread's share of V's rows (raw until used)
+  // -- with kPrefetch the next chunk's inputs load while the current one is
+  // processed (else each chunk loads its own at its start):
+  // this wave's token rows of q (pass B only), k, gk in the operand layout
+  // and this thread's share of V's rows, raw until used
   constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
   Raw8<InT> rq[NKS], rk[NKS], rg[NKS], rv[NIT];
   bool rpad, rvpad[NIT];
-  auto issue = [&](int n) {
+  auto issue = [&](int n, bool with_q) {
     const int rr = token_row(n * C + t, T, gh, gw, dir);
-    const InT* base = nullptr;
     rpad = rr < 0;
     const long row = ((long)b * T + (rr >= 0 ? rr : 0)) * H + h;  // padding reads row 0
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      rq[ks].load(qp + row * DK + 32 * ks + lk);
+      if (with_q) rq[ks].load(qp + row * DK + 32 * ks + lk);
       rk[ks].load(kp + row * DK + 32 * ks + lk);
       rg[ks].load(gp + row * DK + 32 * ks + lk);
     }
@@ -186,22 +170,9 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
       rvpad[it] = vr < 0;
       rv[it].load(vp + (((long)b * T + (vr >= 0 ? vr : 0)) * H + h) * DV + c8);
     }
-    (void)base;
   };
-  issue(run * G);
-
-#pragma nounroll
-  for (int g = 0; g < ng; ++g) {
-    const int n = run * G + g, tok0 = n * C;
-    // -- take this chunk's inputs, then start loading the next chunk's
-    float qf[NEL], kf[NEL], sc[NEL];
-    const bool pad = rpad;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      rq[ks].get(&qf[8 * ks]);
-      rk[ks].get(&kf[8 * ks]);
-      rg[ks].get(&sc[8 * ks]);
-    }
+  // V rows of the current chunk to LDS (zero for padding rows)
+  auto put_v = [&]() {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int u = tid + kThreads * it;
@@ -212,110 +183,87 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
         *reinterpret_cast<half8*>(&sV[r][c8]) = x;
       }
     }
-    if (g + 1 < ng) issue(n + 1);
-    if (tid < DK) sRowMax[tid] = 0u;
-    if (tok0 + C > T) {  // the chain's last chunk: zero the padding rows
-      zero_row<NEL>(pad, qf);
+  };
+  // the largest |x| of this lane's accumulator-layout values into its row
+  auto row_max_into_lds = [&](const floatx4* X) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      if (wave + 4 * i < NBLK) {
+        const float m = fmaxf(fmaxf(fabsf(X[i][0]), fabsf(X[i][1])),
+                              fmaxf(fabsf(X[i][2]), fabsf(X[i][3])));
+        atomicMax(&sRowMax[drow], __float_as_uint(m));
+      }
+    }
+  };
+  // this lane's accumulator-layout values into sXs, rows divided by their scales
+  auto stage_rows = [&](const floatx4* X) {
+    const float inv = inv_scale(row_scale(__uint_as_float(sRowMax[drow])));
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wave + 4 * i;
+      if (blk < NBLK) {
+        const floatx4 x = X[i] * inv;
+        *reinterpret_cast<half4*>(&sXs[drow][16 * (blk / ND) + 4 * lq]) = cvt4(x);
+      }
+    }
+  };
+
+  floatx4 X[BPW];  // pass A: the run's aggregate; pass B: the state S
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) X[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (tid < DK) sWl[tid] = 0.f;
+  if (tid == 0) sPub = 0u;
+  if (kPrefetch) issue(run * G, false);
+
+  // ===== pass A: the run's aggregate
+#pragma nounroll
+  for (int g = 0; g < ng; ++g) {
+    const int tok0 = (run * G + g) * C;
+    if (!kPrefetch) issue(run * G + g, false);
+    float kf[NEL], sc[NEL];
+    const bool pad = rpad;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      rk[ks].get(&kf[8 * ks]);
+      rg[ks].get(&sc[8 * ks]);
+    }
+    put_v();
+    if (kPrefetch) {
+      if (g + 1 < ng) issue(run * G + g + 1, false);
+      else issue(run * G, true);  // pass B's first chunk, during the look-back
+    }
+    if (tok0 + C > T) {
       zero_row<NEL>(pad, kf);
       zero_row<NEL>(pad, sc);
     }
 #pragma unroll
     for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]) * kLog2e;
-    if (lr == 15 || lr == 7) {
+    if (lr == 15) {
 #pragma unroll
-      for (int e = 0; e < NEL; ++e) {
-        const int d = 32 * (e / 8) + lk + (e % 8);
-        if (lr == 15) sTot[I][d] = sc[e];
-        else sS7[I][d] = sc[e];
-      }
+      for (int e = 0; e < NEL; ++e) sTot[I][32 * (e / 8) + lk + (e % 8)] = sc[e];
     }
     __syncthreads();
-
-    // -- per (sub-block, key dim) factors, one key dim per thread
-    if (tid < NB * DK) {
+    if (tid < NB * DK) {  // totals of sub-blocks I..NB-1, the chunk's decay
       const int I2 = tid / DK, d = tid % DK;
-      float tots[NB];
+      float aft = 0.f;
 #pragma unroll
-      for (int J = 0; J < NB; ++J) tots[J] = sTot[J][d];
-      const float s7 = sS7[I2][d];
-      float beta = 0.f, tot = 0.f, after = 0.f;
-#pragma unroll
-      for (int J = 0; J < NB; ++J) {
-        if (J < I2) beta += tots[J];
-        else if (J == I2) tot = tots[J];
-        else after += tots[J];
-      }
-      sEb[I2][d] = fexp2(beta);
-      sEw[I2][d] = fexp2(beta + sWl[d]);
-      sR1[I2][d] = fexp2(-s7);
-      sR2[I2][d] = fexp2(s7 - tot);
-      sF[I2][d] = fexp2(after);
-      float acc = 0.f;
-#pragma unroll
-      for (int J = NB - 2; J >= 0; --J) {
-        if (J < I2) {
-          sM[I2 * (I2 - 1) / 2 + J][d] = fexp2(acc);
-          acc += tots[J];
-        }
-      }
-      if (I2 == NB - 1) {
-        sAn[d] = fexp2(beta + tot);
-        sBt[d] = beta + tot;
-      }
-    }
-    // -- the state X_n (before this chunk) is read out below: its row maxima
-    if (g > 0) {
-#pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        if (wave + 4 * i < NBLK) {
-          const float m = fmaxf(fmaxf(fabsf(X[i][0]), fabsf(X[i][1])),
-                                fmaxf(fabsf(X[i][2]), fabsf(X[i][3])));
-          atomicMax(&sRowMax[drow], __float_as_uint(m));
-        }
+      for (int J = 0; J < NB; ++J) aft += J >= I2 ? sTot[J][d] : 0.f;
+      sF[I2][d] = aft;
+      if (I2 == 0) {
+        sAn[d] = fexp2(aft);
+        sWl[d] += aft;
       }
     }
     __syncthreads();
-
-    // -- per-element factors; K~ and K^ to LDS
-    float qt[NEL], kt[NEL];
-    float rng = 0.f, big = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      float tt[8], ff[8], x1[8], x2[8];
-      lds8(&sTot[I][32 * ks + lk], tt);
-      lds8(&sF[I][32 * ks + lk], ff);
+      float aft[8], x[8];
+      lds8(&sF[I][32 * ks + lk], aft);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int e = 8 * ks + c;
-        rng = fmaxf(rng, -tt[c]);
-        big = fmaxf(big, fmaxf(fabsf(qf[e]), fabsf(kf[e])));
-        qt[e] = qf[e] * fexp2(sc[e]);
-        kt[e] = kf[e] * fexp2(tt[c] - sc[e]);
-        x1[c] = kt[e];
-        x2[c] = kt[e] * ff[c];
-      }
-      *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = cvt8(x1);
-      *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = cvt8(x2);
+      for (int c = 0; c < 8; ++c) x[c] = kf[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]);
+      *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = cvt8(x);
     }
-    // -- stage X_n (rows divided by their scales) for the in-run readout; the
-    // largest row scale by a reduction within each wave (a tile-wide LDS
-    // atomic from every lane would serialize)
-    const float smax_x =
-        g > 0 ? row_scale(group_max<64>(__uint_as_float(sRowMax[lane % DK]))) : 1.f;
-    if (g > 0) {
-#pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        const int blk = wave + 4 * i;
-        if (blk < NBLK) {
-          const int E = blk / ND;
-          const floatx4 x = X[i] * inv_scale(row_scale(__uint_as_float(sRowMax[drow])));
-          *reinterpret_cast<half4*>(&sXs[drow][16 * E + 4 * lq]) = cvt4(x);
-        }
-      }
-    }
-    __syncthreads();  // K~, K^ and X_n in LDS
-
-    // -- U_n into X: X <- diag(a_n) X + K^T V
+    __syncthreads();
     {
       const float an = sAn[drow];
 #pragma unroll
@@ -333,179 +281,15 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
         }
       }
     }
-
-    // -- score sub-blocks (as in the chunk kernel): diagonal by this wave's
-    // tier, off-diagonal on factors <= 1, scaled down by sigA if needed
-    half4 A[NB];
-    float sigA = 1.f;
-    {
-      const float amp = big * fexp2(fminf(rng, 127.f));
-      const int tier = __all(rng <= kHalfRange && amp <= 32768.f)  ? 0
-                       : __all(rng <= kF32Range && amp < 0x1p126f) ? 1
-                                                                    : 2;
-      floatx4 dacc = {0.f, 0.f, 0.f, 0.f};
-      if (tier == 0) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          float r1[8], r2[8], xa[8], xb[8];
-          lds8(&sR1[I][32 * ks + lk], r1);
-          lds8(&sR2[I][32 * ks + lk], r2);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            xa[c] = qt[8 * ks + c] * r1[c];
-            xb[c] = kt[8 * ks + c] * r2[c];
-          }
-          dacc = mfma16x16x32(cvt8(xb), cvt8(xa), dacc);
-        }
-      } else if (tier == 1) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          float r1[8], r2[8];
-          lds8(&sR1[I][32 * ks + lk], r1);
-          lds8(&sR2[I][32 * ks + lk], r2);
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-            dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[8 * ks + c] * r2[c],
-                                                        qt[8 * ks + c] * r1[c], dacc, 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float part = 0.f;
-#pragma unroll
-          for (int e = 0; e < NEL; ++e) {
-            const float kj = __shfl(kf[e], (lane & 48) | j);
-            const float sj = __shfl(sc[e], (lane & 48) | j);
-            part += qf[e] * kj * fexp2(sc[e] - sj);
-          }
-          part += __shfl_xor(part, 16);
-          part += __shfl_xor(part, 32);
-          if ((j >> 2) == lq) dacc[j & 3] = part;
-        }
-      }
-      floatx4 Af[NB];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dacc[r] = (4 * lq + r <= lr) ? dacc[r] : 0.f;
-#pragma unroll
-      for (int J = 0; J < NB; ++J) {
-        if (J == I) Af[J] = dacc;
-        else if (J > I) Af[J] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int J = 0; J < NB - 1; ++J) {
-        if (J < I) {
-          const int pr = I * (I - 1) / 2 + J;
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            float mm[8], x[8];
-            lds8(&sM[pr][32 * ks + lk], mm);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) x[c] = qt[8 * ks + c] * mm[c];
-            const half8 ka = *reinterpret_cast<const half8*>(&sKt[16 * J + lr][32 * ks + lk]);
-            acc = mfma16x16x32(ka, cvt8(x), acc);
-          }
-          Af[J] = acc;
-        }
-      }
-      float am = 0.f;
-#pragma unroll
-      for (int J = 0; J < NB; ++J)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(Af[J][r]));
-      if (__any(am > kRowRange)) {
-        sigA = row_scale(group_max<64>(am));
-        const float inv = inv_scale(sigA);
-#pragma unroll
-        for (int J = 0; J < NB; ++J) Af[J] *= inv;
-      }
-#pragma unroll
-      for (int J = 0; J < NB; ++J) A[J] = cvt4(Af[J]);
-    }
-
-    // -- Q^ for the in-run readout (with X's row scales folded in when a row
-    // is scaled) and the held Q^' = Q^ 2^(W_n)
-    half8 qx[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float eb[8], ew[8], x[8], y[8];
-      lds8(&sEb[I][32 * ks + lk], eb);
-      lds8(&sEw[I][32 * ks + lk], ew);
-      if (smax_x != 1.f) {
-        const float is = inv_scale(smax_x);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          eb[c] *= row_scale(__uint_as_float(sRowMax[32 * ks + lk + c])) * is;
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        x[c] = qt[8 * ks + c] * eb[c];
-        y[c] = qt[8 * ks + c] * ew[c];
-      }
-      qx[ks] = cvt8(x);
-      Qh[G - 1][ks] = cvt8(y);
-    }
-
-    // -- O_n = A V + Q^ X_n
-    {
-      const bool rescale = sigA != 1.f || smax_x != 1.f;
-      const float f1 = sigA * inv_scale(smax_x);
-#pragma unroll
-      for (int E = 0; E < NE; ++E) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J <= I) {
-            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
-            acc = mfma16x16x16(A[J], vb, acc);
-          }
-        }
-        if (g > 0) {
-          if (rescale) acc *= f1;
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const half4 sb = ld_tr<SSTR, 8>(&sXs[32 * ks + 4 * hh][16 * E]);
-              const half4 qa = hh ? __builtin_shufflevector(qx[ks], qx[ks], 4, 5, 6, 7)
-                                  : __builtin_shufflevector(qx[ks], qx[ks], 0, 1, 2, 3);
-              acc = mfma16x16x16(qa, sb, acc);
-            }
-          }
-          if (smax_x != 1.f) acc *= smax_x;
-        } else if (sigA != 1.f) {
-          acc *= sigA;
-        }
-        if constexpr (kHoldHalf) Oh[G - 1][E] = cvt4(acc);
-        else Oh[G - 1][E] = acc;
-      }
-    }
-    __syncthreads();  // every read of this chunk's LDS tiles and factors done
-    if (tid < DK) sWl[tid] += sBt[tid];
-    if (g + 1 < ng) shift();
+    __syncthreads();  // sV, sKh, sF, sAn free for the next chunk
   }
 
   // ===== the run's aggregate X, its decay 2^(W), and the state entering it
   if (tid < DK) sRowMax[tid] = 0u;
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    if (wave + 4 * i < NBLK) {
-      const float m = fmaxf(fmaxf(fabsf(X[i][0]), fabsf(X[i][1])),
-                            fmaxf(fabsf(X[i][2]), fabsf(X[i][3])));
-      atomicMax(&sRowMax[drow], __float_as_uint(m));
-    }
-  }
+  row_max_into_lds(X);
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int blk = wave + 4 * i;
-    if (blk < NBLK) {
-      const int E = blk / ND;
-      const floatx4 x = X[i] * inv_scale(row_scale(__uint_as_float(sRowMax[drow])));
-      *reinterpret_cast<half4*>(&sXs[drow][16 * E + 4 * lq]) = cvt4(x);
-    }
-  }
+  stage_rows(X);
   if (tid < DK) {
     sSig[tid] = row_scale(__uint_as_float(sRowMax[tid]));
     sAn[tid] = fexp2(sWl[tid]);  // the run's decay
@@ -514,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
 
   const __amdgpu_buffer_rsrc_t rA = coh_rsrc(AggT + (long)ch * NS * DKDV, (long)NS * DKDV);
   const __amdgpu_buffer_rsrc_t rI = coh_rsrc(IncT + (long)ch * NS * DKDV, (long)NS * DKDV);
-  float xs[NGR][8];  // the state entering the run, then the inclusive state
+  float xs[NGR][8];  // the state entering the run (group layout: 8 elements of one row)
   if (run > 0) {
     // -- publish the aggregate
 #pragma unroll
@@ -635,17 +419,14 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
   // -- publish the inclusive state A_run S_in + X (for the next runs, or as
   // the final state), then count this run as done reading
   const bool last = run == NS - 1;
-  float sin_m[NGR];
 #pragma unroll
   for (int gr = 0; gr < NGR; ++gr) {
     const int x8 = 8 * (tid + kThreads * gr), d = x8 / DV;
-    sin_m[gr] = 0.f;
     if (x8 < DKDV) {
       const half8 ag = *reinterpret_cast<const half8*>(&sXs[d][x8 % DV]);
       float inc[8], m = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        sin_m[gr] = fmaxf(sin_m[gr], fabsf(xs[gr][c]));
         inc[c] = sAn[d] * xs[gr][c] + sSig[d] * (float)ag[c];
         m = fmaxf(m, fabsf(inc[c]));
       }
@@ -672,74 +453,273 @@ __global__ __launch_bounds__(kThreads, 2) void runs_kernel(
     for (int i = tid; i < NS + 1; i += kThreads) cw[i] = 0u;
   }
 
-  // -- stage S_in (rows divided by their scales) and finish the held chunks
-  __syncthreads();
+  // ===== pass B: S_in into the accumulator layout (through LDS in float),
+  // then every chunk in full with S carried along the run
 #pragma unroll
   for (int gr = 0; gr < NGR; ++gr) {
-    const int x8 = 8 * (tid + kThreads * gr), d = x8 / DV;
-    if (x8 < DKDV) {
-      const float sg = row_scale(DV == 64 ? group_max<8>(sin_m[gr]) : group_max<4>(sin_m[gr]));
-      const float inv = inv_scale(sg);
-      float o[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] = xs[gr][c] * inv;
-      *reinterpret_cast<half8*>(&sXs[d][x8 % DV]) = cvt8(o);
-      if (x8 % DV == 0) sSig[d] = sg;
-    }
+    const int x8 = 8 * (tid + kThreads * gr);
+    if (x8 < DKDV) store_f8(&sS32[x8 / DV][x8 % DV], xs[gr]);
   }
   __syncthreads();
-  const float smax = group_max<64>(sSig[lane % DK]);
-  // the held chunks sit in slots G-ng .. G-1, oldest first: bring the
-  // oldest to slot 0, then take slot 0 and shift, once per chunk
-#pragma nounroll
-  for (int j = ng; j < G; ++j) shift();
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + 4 * i;
+    if (blk < NBLK)
+      X[i] = *reinterpret_cast<const floatx4*>(&sS32[drow][16 * (blk / ND) + 4 * lq]);
+  }
+  __syncthreads();  // sS32 read; its region becomes K^ and S again
+
 #pragma nounroll
   for (int g = 0; g < ng; ++g) {
-    half8 qs[NKS];
+    const int tok0 = (run * G + g) * C;
+    if (!kPrefetch) issue(run * G + g, true);
+    float qf[NEL], kf[NEL], sc[NEL];
+    const bool pad = rpad;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qs[ks] = Qh[0][ks];
-    if (smax != 1.f) {
-      const float is = inv_scale(smax);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        float f[8], x[8];
-        lds8(&sSig[32 * ks + lk], f);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[c] = (float)qs[ks][c] * (f[c] * is);
-        qs[ks] = cvt8(x);
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      rq[ks].get(&qf[8 * ks]);
+      rk[ks].get(&kf[8 * ks]);
+      rg[ks].get(&sc[8 * ks]);
+    }
+    put_v();
+    if (kPrefetch && g + 1 < ng) issue(run * G + g + 1, true);
+    if (tid < DK) sRowMax[tid] = 0u;
+    if (tok0 + C > T) {
+      zero_row<NEL>(pad, qf);
+      zero_row<NEL>(pad, kf);
+      zero_row<NEL>(pad, sc);
     }
 #pragma unroll
-    for (int E = 0; E < NE; ++E) {
-      floatx4 acc;
-      if constexpr (kHoldHalf) acc = __builtin_convertvector(Oh[0][E], floatx4);
-      else acc = Oh[0][E];
-      if (smax != 1.f) acc *= inv_scale(smax);
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]) * kLog2e;
+    if (lr == 15 || lr == 7) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const half4 sb = ld_tr<SSTR, 8>(&sXs[32 * ks + 4 * hh][16 * E]);
-          const half4 qa = hh ? __builtin_shufflevector(qs[ks], qs[ks], 4, 5, 6, 7)
-                              : __builtin_shufflevector(qs[ks], qs[ks], 0, 1, 2, 3);
-          acc = mfma16x16x16(qa, sb, acc);
-        }
+      for (int e = 0; e < NEL; ++e) {
+        const int d = 32 * (e / 8) + lk + (e % 8);
+        if (lr == 15) sTot[I][d] = sc[e];
+        else sS7[I][d] = sc[e];
       }
-      if (smax != 1.f) acc *= smax;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (InT)acc[r];
     }
     __syncthreads();
-    // scatter the chunk's rows to their raster positions
-    const int tok0 = (run * G + g) * C;
+    row_max_into_lds(X);  // rows of the state entering this chunk
+    // -- per (sub-block, key dim) factors, one key dim per thread
+    if (tid < NB * DK) {
+      const int I2 = tid / DK, d = tid % DK;
+      float tots[NB];
+#pragma unroll
+      for (int J = 0; J < NB; ++J) tots[J] = sTot[J][d];
+      const float s7 = sS7[I2][d];
+      float beta = 0.f, tot = 0.f, after = 0.f;
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        if (J < I2) beta += tots[J];
+        else if (J == I2) tot = tots[J];
+        else after += tots[J];
+      }
+      sEb[I2][d] = fexp2(beta);
+      sR1[I2][d] = fexp2(-s7);
+      sR2[I2][d] = fexp2(s7 - tot);
+      sF[I2][d] = fexp2(after);
+      float acc = 0.f;
+#pragma unroll
+      for (int J = NB - 2; J >= 0; --J) {
+        if (J < I2) {
+          sM[I2 * (I2 - 1) / 2 + J][d] = fexp2(acc);
+          acc += tots[J];
+        }
+      }
+      if (I2 == NB - 1) sAn[d] = fexp2(beta + tot);
+    }
+    __syncthreads();
+    // -- S_n into LDS (rows divided by their scales) for the readout
+    stage_rows(X);
+    if (tid < DK) sSig[tid] = row_scale(__uint_as_float(sRowMax[tid]));
+    // -- per-element factors; K~ and K^ to LDS
+    float qt[NEL], kt[NEL];
+    float rng = 0.f, big = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float tt[8], ff[8], x1[8], x2[8];
+      lds8(&sTot[I][32 * ks + lk], tt);
+      lds8(&sF[I][32 * ks + lk], ff);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int e = 8 * ks + c;
+        rng = fmaxf(rng, -tt[c]);
+        big = fmaxf(big, fmaxf(fabsf(qf[e]), fabsf(kf[e])));
+        qt[e] = qf[e] * fexp2(sc[e]);
+        kt[e] = kf[e] * fexp2(tt[c] - sc[e]);
+        x1[c] = kt[e];
+        x2[c] = kt[e] * ff[c];
+      }
+      *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = cvt8(x1);
+      *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = cvt8(x2);
+    }
+    __syncthreads();  // K~, K^, S_n and its row scales in LDS
+
+    // -- score sub-blocks: diagonal by this wave's tier, off-diagonal on
+    // factors <= 1, scaled down by sigA if needed
+    half4 A[NB];
+    float sigA = 1.f;
+    {
+      const float amp = big * fexp2(fminf(rng, 127.f));
+      const int tier = __all(rng <= kHalfRange && amp <= 32768.f)  ? 0
+                       : __all(rng <= kF32Range && amp < 0x1p126f) ? 1
+                                                                    : 2;
+      floatx4 dacc = {0.f, 0.f, 0.f, 0.f};
+      if (tier == 0) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          float r1[8], r2[8], xa[8], xb[8];
+          lds8(&sR1[I][32 * ks + lk], r1);
+          lds8(&sR2[I][32 * ks + lk], r2);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            xa[c] = qt[8 * ks + c] * r1[c];
+            xb[c] = kt[8 * ks + c] * r2[c];
+          }
+          dacc = mfma16x16x32(cvt8(xb), cvt8(xa), dacc);
+        }
+      } else if (tier == 1) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          float r1[8], r2[8];
+          lds8(&sR1[I][32 * ks + lk], r1);
+          lds8(&sR2[I][32 * ks + lk], r2);
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[8 * ks + c] * r2[c],
+                                                        qt[8 * ks + c] * r1[c], dacc, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < NEL; ++e) {
+            const float kj = __shfl(kf[e], (lane & 48) | j);
+            const float sj = __shfl(sc[e], (lane & 48) | j);
+            part += qf[e] * kj * fexp2(sc[e] - sj);
+          }
+          part += __shfl_xor(part, 16);
+          part += __shfl_xor(part, 32);
+          if ((j >> 2) == lq) dacc[j & 3] = part;
+        }
+      }
+      floatx4 Af[NB];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dacc[r] = (4 * lq + r <= lr) ? dacc[r] : 0.f;
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        if (J == I) Af[J] = dacc;
+        else if (J > I) Af[J] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int J = 0; J < NB - 1; ++J) {
+        if (J < I) {
+          const int pr = I * (I - 1) / 2 + J;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            float mm[8], x[8];
+            lds8(&sM[pr][32 * ks + lk], mm);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = qt[8 * ks + c] * mm[c];
+            const half8 ka = *reinterpret_cast<const half8*>(&sKt[16 * J + lr][32 * ks + lk]);
+            acc = mfma16x16x32(ka, cvt8(x), acc);
+          }
+          Af[J] = acc;
+        }
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int J = 0; J < NB; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(Af[J][r]));
+      if (__any(am > kRowRange)) {
+        sigA = row_scale(group_max<64>(am));
+        const float inv = inv_scale(sigA);
+#pragma unroll
+        for (int J = 0; J < NB; ++J) Af[J] *= inv;
+      }
+#pragma unroll
+      for (int J = 0; J < NB; ++J) A[J] = cvt4(Af[J]);
+    }
+    // -- Q^ = q 2^(b_i), with S_n's row scales folded in when a row is scaled
+    const float smax = group_max<64>(sSig[lane % DK]);
+    half8 qh[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float eb[8], x[8];
+      lds8(&sEb[I][32 * ks + lk], eb);
+      if (smax != 1.f) {
+        float f[8];
+        lds8(&sSig[32 * ks + lk], f);
+        const float is = inv_scale(smax);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) eb[c] *= f[c] * is;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[c] = qt[8 * ks + c] * eb[c];
+      qh[ks] = cvt8(x);
+    }
+    // -- the state after this chunk: S <- diag(a_n) S + K^T V
+    {
+      const float an = sAn[drow];
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int blk = wave + 4 * i;
+        if (blk < NBLK) {
+          const int E = blk / ND, D = blk % ND;
+          X[i] *= an;
+#pragma unroll
+          for (int J = 0; J < NB; ++J) {
+            const half4 a = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
+            const half4 bb = ld_tr<HSTR, 4>(&sKh[16 * J][16 * D]);
+            X[i] = mfma16x16x16(a, bb, X[i]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // K~ is no longer read: its LDS becomes the output tile
+    // -- O = A V + Q^ S_n
+    {
+      const bool rescale = sigA != 1.f || smax != 1.f;
+      const float f1 = sigA * inv_scale(smax);
+#pragma unroll
+      for (int E = 0; E < NE; ++E) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+          if (J <= I) {
+            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
+            acc = mfma16x16x16(A[J], vb, acc);
+          }
+        }
+        if (rescale) acc *= f1;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const half4 sb = ld_tr<SSTR, 8>(&sXs[32 * ks + 4 * hh][16 * E]);
+            const half4 qa = hh ? __builtin_shufflevector(qh[ks], qh[ks], 4, 5, 6, 7)
+                                : __builtin_shufflevector(qh[ks], qh[ks], 0, 1, 2, 3);
+            acc = mfma16x16x16(qa, sb, acc);
+          }
+        }
+        if (smax != 1.f) acc *= smax;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sO[16 * I + 4 * lq + r][16 * E + lr] = (InT)acc[r];
+      }
+    }
+    __syncthreads();
+    // -- scatter the chunk's rows to their raster positions
     constexpr int LPR = DV / 8;
     for (int u = tid; u < C * LPR; u += kThreads) {
       const int r = u / LPR, c8 = (u % LPR) * 8;
       const int rr = token_row(tok0 + r, T, gh, gw, dir);
       if (rr >= 0) copy8(op + (((long)b * T + rr) * H + h) * DV + c8, &sO[r][c8]);
     }
-    __syncthreads();
-    shift();
+    __syncthreads();  // every LDS tile of this chunk is free
   }
 }
 

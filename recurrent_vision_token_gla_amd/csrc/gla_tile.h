@@ -144,6 +144,15 @@ __device__ __forceinline__ float row_scale(float m) {
   const int e = eb - 140;  // m < 2^(eb-126), so m / 2^e < 2^14
   return (e <= 0 || eb == 255) ? 1.f : __uint_as_float((unsigned)(e + 127) << 23);
 }
+// A value the caller knows to be equal on every lane, made a scalar so that
+// branches on it are scalar branches (the compiler cannot see the equality).
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
 // 1 / sigma, exact (sigma is a power of two between 1 and 2^114)
 __device__ __forceinline__ float inv_scale(float sigma) {
   return __uint_as_float(((254u << 23) - __float_as_uint(sigma)) & 0x7f800000u);
