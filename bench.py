@@ -3,8 +3,11 @@
 
 Metric: forward tokens/s (fp16) on the 640x640-image workload (B=1, 40x40
 stride-16 grid = 1,600 tokens, H=6, dk=dv=64, chunk 64, one call per scan
-direction), with the 1280x1280 workload (6,400 tokens) reported beside it,
-and the fraction of the HBM roofline reached.
+direction), with the other fp16 workloads reported beside it (the 1280x1280
+image: 6,400 tokens; eight 640x640 images at H=12; the 12-block
+direction-cycling stack over four 1280x1280 images at H=16), each with the
+fraction of the HBM roofline reached by the path and by its dominant kernel,
+and the counter-measured traffic where the kernel sources match it.
 
 A step is one pass of the workload: one gla_fwd call per scan direction on
 that call's own seeded inputs, already resident in device memory. Steps are
@@ -15,7 +18,7 @@ through copies of the step's inputs and outputs that together exceed twice
 the 256 MB Infinity Cache, so the bytes come from HBM; the same steps on one
 set of buffers (cache-warm) are reported beside it. One JSON line is printed.
 
-  python bench.py [--steps K] [--warmup W] [--workload I] [--all]
+  python bench.py [--steps K] [--warmup W] [--workload I] [--no-also]
 """
 from __future__ import annotations
 
@@ -37,7 +40,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores, published
 ROTATE_BYTES = 512 << 20  # rotating buffers: twice the 256 MB Infinity Cache
 MAX_SETS = 64
 KERNEL_SOURCES = ["gla_kernels.hip", "gla_chunk.h", "gla_tile.h", "gla_gated.hip",
-                  "ssw_kernels.hip", "gla_device.h", "gla_launch.h"]
+                  "gla_runs.hip", "ssw_kernels.hip", "gla_device.h", "gla_launch.h"]
 
 
 def source_sha() -> str:
@@ -61,18 +64,22 @@ def phase_bytes(w):
     single_pass: read q, k, gk, v; write o (the whole forward's own I/O; the
                  chunk summaries it publishes to its successors are not
                  counted)
-    summaries:   read k, gk, v; write U (f16 dk*dv) and a (f32 dk) per chunk-head
-    scan:        read U and a; write S (f16 dk*dv) per chunk-head
-    outputs:     read q, k, gk, v and S; write o
+    runs:        the same (one launch; its published run states not counted)
+    summaries:   read k, gk, v; write per chunk-head U (f16 dk*dv) and the
+                 pairs (a, row max of U) (2 f32 per key dim)
+    scan:        read U and the pairs; write S (f16 dk*dv) and its row
+                 scales (f32 dk)
+    outputs:     read q, k, gk, v, S and its row scales; write o
     """
     e = 2 if w.dtype == "f16" else 4
     th = w.B * w.T * w.H
     ch = w.B * w.H * math.ceil(w.T / w.chunk)
     return {
         "single_pass": th * per_unit_bytes(w),
-        "summaries": th * (2 * w.dk + w.dv) * e + ch * (2 * w.dk * w.dv + 4 * w.dk),
-        "scan": ch * (2 * w.dk * w.dv + 4 * w.dk + 2 * w.dk * w.dv),
-        "outputs": th * (3 * w.dk + 2 * w.dv) * e + ch * 2 * w.dk * w.dv,
+        "runs": th * per_unit_bytes(w),
+        "summaries": th * (2 * w.dk + w.dv) * e + ch * (2 * w.dk * w.dv + 8 * w.dk),
+        "scan": ch * (2 * w.dk * w.dv + 8 * w.dk + 2 * w.dk * w.dv + 4 * w.dk),
+        "outputs": th * (3 * w.dk + 2 * w.dv) * e + ch * (2 * w.dk * w.dv + 4 * w.dk),
     }
 
 
@@ -84,8 +91,8 @@ def phase_flops(w):
     th = w.B * w.T * w.H
     summ = 2 * w.dk * w.dv
     outs = 2 * w.dk * w.dv + w.chunk * (w.dk + w.dv)
-    return {"single_pass": th * (summ + outs), "summaries": th * summ, "scan": 0,
-            "outputs": th * outs}
+    return {"single_pass": th * (summ + outs), "runs": th * (summ + outs),
+            "summaries": th * summ, "scan": 0, "outputs": th * outs}
 
 
 def load_traffic(kernel: str, workload: str):
@@ -103,6 +110,18 @@ def load_traffic(kernel: str, workload: str):
                 return None
             return r.get("hbm_bytes_per_launch")
     return None
+
+
+def path_traffic(w, used):
+    """Counter-measured HBM bytes of one call (the sum over the kernels its
+    schedule launches) and their ratio to the path's algorithmic bytes, or
+    None when any of them is missing or stale."""
+    parts = [load_traffic(k, w.name) for k in used]
+    if any(x is None for x in parts):
+        return None
+    path = w.B * w.T * w.H * per_unit_bytes(w)
+    return {"bytes_per_call": sum(parts), "ratio": sum(parts) / path,
+            "kernels": dict(zip(used, parts))}
 
 
 def _graph(torch, stream, fn):
@@ -189,14 +208,15 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
     # back to back in one graph (no host gaps) on the rotating sets, timed
     # with events on the stream the kernels are launched on; and the same on
     # the first set alone. The step's own schedule is the one gla_fwd picks;
-    # the other schedule's kernels are timed for reference.
+    # the other schedules' kernels are timed for reference.
     sched = gla.auto_schedule(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk)
 
     def phase(name, c0, s):
-        if name == "single_pass":
+        if name in ("single_pass", "runs"):
             return gla.fwd(c0["q"], c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w, c0["dirs"],
                            w.chunk, out=c0["out"], workspace=ws, stream=s,
-                           schedule=gla.SCHED_SINGLE_PASS)
+                           schedule=gla.SCHED_SINGLE_PASS if name == "single_pass"
+                           else gla.SCHED_RUNS)
         if name == "summaries":
             return gla.chunk_summaries(c0["k"], c0["v"], c0["g"], w.grid_h, w.grid_w, c0["dirs"],
                                        w.chunk, workspace=ws, stream=s)
@@ -222,8 +242,8 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
         return a.elapsed_time(b) * 1e3 / (3 * timing_reps)
 
     phase_us, phase_warm_us = {}, {}
-    for name in ("single_pass", "summaries", "scan", "outputs"):
-        if name == "single_pass":
+    for name in ("single_pass", "runs", "summaries", "scan", "outputs"):
+        if name in ("single_pass", "runs"):
             try:
                 phase(name, calls[0], None)  # rejected on the host (nothing launched) if it does not fit
             except gla.GLAError:
@@ -409,6 +429,7 @@ def summarize(w, res):
                           "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
                           "kernel": dom, "algorithmic_flops_per_launch": fl[dom],
                           "path_frac": path_flops / (call_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS},
+        "path_traffic": path_traffic(w, res["used"]),
         "phase_us": res["phase_us"],
         "schedule": res["schedule"],
         "warm": {"value": tokens_step / (res["warm_ms_per_step"] * 1e-3),
@@ -425,7 +446,6 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1, help="index into workloads.WORKLOADS")
-    ap.add_argument("--all", action="store_true", help="also run the batched and stack workloads")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -484,9 +504,9 @@ def main():
               file=sys.stderr, flush=True)
 
     also = []
-    extra = [2] if args.workload == 1 and not args.no_also else []
-    if args.all:
-        extra += [i for i in (2, 3, 4) if i != args.workload and i not in extra]
+    # the other fp16 image workloads: 80x80 (6,400 tokens), eight 40x40 images
+    # at H 12, and the 12-block stack of four 80x80 images at H 16
+    extra = [i for i in (2, 3, 4) if i != args.workload] if not args.no_also else []
     for i in extra:
         wi = W.WORKLOADS[i]
         ri = run_workload(wi, max(10, args.steps // 4), max(3, args.warmup // 4),
@@ -501,7 +521,9 @@ def main():
                      "value": si["value"], "unit": "tokens/s", "us_per_call": si["call_us"],
                      "path_roofline_frac": si["path_roofline"]["frac"],
                      "schedule": si["schedule"], "dominant": si["dominant"],
-                     "dominant_frac": si["roofline"]["frac"], "kernel_us": si["phase_us"],
+                     "dominant_frac": si["roofline"]["frac"],
+                     "dominant_traffic": si["roofline"]["traffic"],
+                     "path_traffic": si["path_traffic"], "kernel_us": si["phase_us"],
                      "warm": si["warm"], "rotation": si["rotation"]})
         del ri
         torch.cuda.empty_cache()
@@ -537,6 +559,7 @@ def main():
                    "timing": "eager" if args.no_graph else "graph_replay"},
         "roofline": s["roofline"],
         "path_roofline": s["path_roofline"],
+        "path_traffic": s["path_traffic"],
         "mfma_roofline": s["mfma_roofline"],
         "median_step_latency_us": s["median_step_latency_us"],
         "schedule": s["schedule"],

@@ -33,9 +33,13 @@ def test_three_phase_bytes_per_launch(bench):
     w = W.WORKLOADS[2]
     th, ch = w.B * w.T * w.H, w.B * w.H * (w.T // w.chunk)
     pb = bench.phase_bytes(w)
-    assert pb["summaries"] == th * 3 * 128 + ch * (8192 + 256)        # k, gk, v in; U, a out
-    assert pb["scan"] == ch * (8192 + 256 + 8192)                      # U, a in; S out
-    assert pb["outputs"] == th * 5 * 128 + ch * 8192                   # q, k, gk, v in, o out; S in
+    # k, gk, v in; U and the (a, row max) pairs out
+    assert pb["summaries"] == th * 3 * 128 + ch * (8192 + 512)
+    # U and the pairs in; S and its row scales out
+    assert pb["scan"] == ch * (8192 + 512 + 8192 + 256)
+    # q, k, gk, v in, o out; S and its row scales in
+    assert pb["outputs"] == th * 5 * 128 + ch * (8192 + 256)
+    assert pb["runs"] == pb["single_pass"]
     fl = bench.phase_flops(w)
     assert fl["summaries"] + fl["outputs"] == fl["single_pass"] and fl["scan"] == 0
 
