@@ -105,7 +105,8 @@ enum {
   GLA_SCHED_AUTO = 0,
   GLA_SCHED_SINGLE_PASS = 1,  /* one workgroup per chunk, segmented look-back */
   GLA_SCHED_THREE_PHASE = 2,  /* summaries, boundary scan, outputs */
-  GLA_SCHED_RUNS = 3          /* one workgroup per run of 4 chunks, decoupled look-back */
+  GLA_SCHED_RUNS = 3          /* one workgroup per run of 4 (fp16) or 3 (fp32) chunks,
+                                 decoupled look-back between runs */
 };
 enum {
   GLA_OK = 0,
@@ -229,11 +230,17 @@ int gla_fwd_noalloc(const void* q, const void* k, const void* v, const void* gk,
                     void* stream);
 
 /* gla_fwd_state with an explicit schedule: GLA_SCHED_AUTO (what gla_fwd and
- * gla_fwd_state do), GLA_SCHED_SINGLE_PASS or GLA_SCHED_THREE_PHASE. The
- * single pass returns GLA_E_UNPREPARED on a workspace gla_workspace_init has
- * not prepared, and GLA_E_UNSUPPORTED if the problem does not fit its control
- * words (more than 4096 chunks per chain, or more chunk-heads per launch than
- * the 64 KiB hold) or if s_final is s0. Results agree up to rounding. */
+ * gla_fwd_state do), GLA_SCHED_SINGLE_PASS, GLA_SCHED_THREE_PHASE or
+ * GLA_SCHED_RUNS. The single pass returns GLA_E_UNPREPARED on a workspace
+ * gla_workspace_init has not prepared, and GLA_E_UNSUPPORTED if the problem
+ * does not fit its control words (more than 4096 chunks per chain, or more
+ * chunk-heads per launch than the 64 KiB hold) or if s_final is s0. The runs
+ * schedule (one workgroup per run of consecutive 64-token chunks of a chain,
+ * the run's chunks exchanging their states through LDS, a decoupled
+ * look-back between runs) takes the same workspace preparation, supports
+ * chunk 64 only, and returns GLA_E_UNSUPPORTED for other chunk sizes, for
+ * s_final equal to s0, with an output gate, or when its per-run words do not
+ * fit the 64 KiB. Results agree up to rounding. */
 int gla_fwd_schedule(const void* q, const void* k, const void* v,
                      const void* gk, void* o, int B, int H, int grid_h,
                      int grid_w, int dk, int dv, const int32_t* dir, int chunk,

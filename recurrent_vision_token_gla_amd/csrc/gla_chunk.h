@@ -56,8 +56,8 @@ namespace tile {
 //      (the other chunks compute theirs while the aggregates arrive);
 //   3. adds the readout Q^ S_n and stores the outputs.
 // ===========================================================================
-template <int DK, int DV, int C, typename InT, bool kFused, bool kGate>
-__global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
+template <int DK, int DV, int C, typename InT, bool kFused, bool kGate, int GR = 1>
+__global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     const InT* __restrict__ qp, const InT* __restrict__ kp, const InT* __restrict__ vp,
     const InT* __restrict__ gp, InT* __restrict__ op, half_t* __restrict__ Uws,
     float* __restrict__ Aws, half_t* __restrict__ Sws, const float* __restrict__ SigS,
@@ -82,20 +82,41 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // one region in turn holds K^, the U staging tile and S (only S unfused)
   constexpr int X0 = DK * SSTR * 2, X1 = kFused ? C * HSTR * 2 : 0, X2 = kFused ? DK * USTR * 2 : 0;
   constexpr int X_BYTES = X0 > X1 ? (X0 > X2 ? X0 : X2) : (X1 > X2 ? X1 : X2);
-  __shared__ __attribute__((aligned(16))) char sKO[KO_BYTES];
-  __shared__ __attribute__((aligned(16))) half_t sV[C][VSTR];
-  __shared__ __attribute__((aligned(16))) char sX[X_BYTES];
-  __shared__ __attribute__((aligned(16))) float sTot[NB][DK], sS7[NB][DK];
-  __shared__ __attribute__((aligned(16))) float sEb[NB][DK], sR1[NB][DK], sR2[NB][DK];
-  __shared__ __attribute__((aligned(16))) float sM[NPAIR > 0 ? NPAIR : 1][DK];
-  __shared__ __attribute__((aligned(16))) float sF[kFused ? NB : 1][DK];  // K^ = K~ * sF
-  __shared__ float sAn[kFused ? DK : 1];
-  __shared__ int sRow[C];
-  __shared__ float sSig[DK];  // row scales of S_n
-  __shared__ float sSigMax;
-  __shared__ unsigned sRowMax[kFused ? DK : 1];  // single pass: row maxima of U_n
-  __shared__ float sSigU[kFused ? DK : 1];       // single pass: row scales of U_n
-  __shared__ unsigned sDone, sPub;
+  // LDS: one block of the tiles below per chunk of the workgroup (GR of them)
+  constexpr int TAB = NB * DK * 4;  // bytes of one [sub-block][key dim] float table
+  constexpr int L_V = lds_round(KO_BYTES), L_X = lds_round(L_V + C * VSTR * 2);
+  constexpr int L_TAB = lds_round(L_X + X_BYTES);  // sTot, sS7, sEb, sR1, sR2
+  constexpr int L_M = L_TAB + 5 * TAB, L_F = L_M + (NPAIR > 0 ? NPAIR : 1) * DK * 4;
+  constexpr int L_AN = L_F + (kFused ? NB : 1) * DK * 4, L_ROW = L_AN + (kFused ? DK : 1) * 4;
+  constexpr int L_SIG = L_ROW + C * 4, L_RMAX = L_SIG + DK * 4;
+  constexpr int L_SIGU = L_RMAX + (kFused ? DK : 1) * 4, L_W = L_SIGU + (kFused ? DK : 1) * 4;
+  constexpr int PER = lds_round(L_W + 16);
+  static_assert(GR * PER <= 160 * 1024, "the chunks of a workgroup exceed the LDS of a CU");
+  __shared__ __attribute__((aligned(16))) char sL[GR * PER];
+  __shared__ int sLook[2];  // runs: the look-back's result, for the whole workgroup
+  const int grp = GR > 1 ? (int)threadIdx.x / kThreads : 0;  // this thread's chunk in the workgroup
+  char* const lb = sL + grp * PER;
+  char(&sKO)[KO_BYTES] = *reinterpret_cast<char(*)[KO_BYTES]>(lb);
+  half_t(&sV)[C][VSTR] = *reinterpret_cast<half_t(*)[C][VSTR]>(lb + L_V);
+  char(&sX)[X_BYTES] = *reinterpret_cast<char(*)[X_BYTES]>(lb + L_X);
+  float(&sTot)[NB][DK] = *reinterpret_cast<float(*)[NB][DK]>(lb + L_TAB);
+  float(&sS7)[NB][DK] = *reinterpret_cast<float(*)[NB][DK]>(lb + L_TAB + TAB);
+  float(&sEb)[NB][DK] = *reinterpret_cast<float(*)[NB][DK]>(lb + L_TAB + 2 * TAB);
+  float(&sR1)[NB][DK] = *reinterpret_cast<float(*)[NB][DK]>(lb + L_TAB + 3 * TAB);
+  float(&sR2)[NB][DK] = *reinterpret_cast<float(*)[NB][DK]>(lb + L_TAB + 4 * TAB);
+  float(&sM)[NPAIR > 0 ? NPAIR : 1][DK] =
+      *reinterpret_cast<float(*)[NPAIR > 0 ? NPAIR : 1][DK]>(lb + L_M);
+  float(&sF)[kFused ? NB : 1][DK] = *reinterpret_cast<float(*)[kFused ? NB : 1][DK]>(lb + L_F);  // K^ = K~ * sF
+  float(&sAn)[kFused ? DK : 1] = *reinterpret_cast<float(*)[kFused ? DK : 1]>(lb + L_AN);
+  int(&sRow)[C] = *reinterpret_cast<int(*)[C]>(lb + L_ROW);
+  float(&sSig)[DK] = *reinterpret_cast<float(*)[DK]>(lb + L_SIG);  // row scales of S_n
+  // single pass: row maxima and row scales of U_n
+  unsigned(&sRowMax)[kFused ? DK : 1] = *reinterpret_cast<unsigned(*)[kFused ? DK : 1]>(lb + L_RMAX);
+  float(&sSigU)[kFused ? DK : 1] = *reinterpret_cast<float(*)[kFused ? DK : 1]>(lb + L_SIGU);
+  float& sSigMax = *reinterpret_cast<float*>(lb + L_W);
+  unsigned& sDone = *reinterpret_cast<unsigned*>(lb + L_W + 4);
+  unsigned& sPub = *reinterpret_cast<unsigned*>(lb + L_W + 8);
+  unsigned& sPub2 = *reinterpret_cast<unsigned*>(lb + L_W + 12);
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
   // The outputs are produced transposed (O^T = V^T A^T + S^T Q^T: the same
@@ -103,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   // four consecutive value columns 16E + 4lq + r of its token 16I + lr and
   // stages them with one 8-byte (16-byte for float) LDS write into token rows.
   auto stage_out = [&](const floatx4& acc, int E) {
-    const int I = threadIdx.x >> 6, lq = (threadIdx.x >> 4) & 3, lr = threadIdx.x & 15;
+    const int I = (threadIdx.x >> 6) % 4, lq = (threadIdx.x >> 4) & 3, lr = threadIdx.x & 15;
     if constexpr (sizeof(InT) == 2) {
       *reinterpret_cast<half4*>(&sO[16 * I + lr][16 * E + 4 * lq]) = cvt4(acc);
     } else {
@@ -113,23 +134,53 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   half_t (*sS)[SSTR] = reinterpret_cast<half_t (*)[SSTR]>(sX);
   half_t (*sKh)[HSTR] = reinterpret_cast<half_t (*)[HSTR]>(sX);
   half_t (*sU)[USTR] = reinterpret_cast<half_t (*)[USTR]>(sX);
+  // runs: the state after the first `upto` chunks of the workgroup's run
+  // when it enters at zero, x = sum_{m < upto} (prod_{m < i < upto} a_i) U_m
+  // (elements x8..x8+7 of row d = x8 / DV, from the chunks' U tiles in LDS),
+  // and the decay w = prod_{m < upto} a_m of that row
+  auto run_prefix = [&](int upto, int x8, float (&x)[8], float& w) {
+    const int d = x8 / DV;
+    w = 1.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = 0.f;
+#pragma unroll
+    for (int m = 0; m < GR; ++m) {
+      if (m < upto) {
+        const char* lm = sL + m * PER;
+        const float am = reinterpret_cast<const float*>(lm + L_AN)[d];
+        const float su = reinterpret_cast<const float*>(lm + L_SIGU)[d];
+        const half8 u = *reinterpret_cast<const half8*>(
+            reinterpret_cast<const half_t*>(lm + L_X) + d * USTR + x8 % DV);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = fmaf(su, (float)u[c], am * x[c]);
+        w *= am;
+      }
+    }
+  };
 
   int n, h, b;
-  if constexpr (kFused) {
+  int run = 0;  // runs: this workgroup's run of GR chunks (nseg = runs per chain)
+  if constexpr (GR > 1) {
+    // run-major: every chain's run 0, then every chain's run 1, ...
+    const int nch = (int)(gridDim.x / nseg);
+    run = blockIdx.x / nch;
+    const int ch = blockIdx.x - run * nch;
+    n = run * GR + grp, h = ch % H, b = ch / H;
+  } else if constexpr (kFused) {
     const int bh = blockIdx.x / N;
     n = blockIdx.x - bh * N, h = bh % H, b = bh / H;
   } else {
     n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   }
   const long bh = (long)b * H + h, bhn = bh * N + n;
-  const int tid = threadIdx.x;
+  const int tid = GR > 1 ? (int)threadIdx.x % kThreads : (int)threadIdx.x;  // within the chunk
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
   const int dir = dirs.get(b);
   // the row table (for the scatter) and the flags below are first read after
   // the barrier that follows the cumulative sums
-  chunk_rows<C>(sRow, n * C, T, gh, gw, dir);
-  if (tid == 0) sPub = 0u;
+  chunk_rows<C>(sRow, n * C, T, gh, gw, dir, tid);
+  if (tid == 0) sPub = 0u, sPub2 = 0u;
   if (kFused && tid < DK) sRowMax[tid] = 0u;
 
   // -- this wave's token rows of q, k, gk in the operand layout (waves past
@@ -158,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     for (int it = 0; it < NSIT; ++it) h8[it] = load8h(Sb + 8 * ((tid + kThreads * it) % (DKDV / 8)));
     sig_d = SigS[bhn * DK + (tid % DK)];
   }
-  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV);
+  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV, tid);
   if constexpr (!kFused) {
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) {
@@ -262,11 +313,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
   __syncthreads();
 
   unsigned* cw = nullptr;  // this chain's control words
-  // this chain's summaries and segment aggregates (single pass only)
-  const __amdgpu_buffer_rsrc_t rU = coh_rsrc(Uws + bh * N * DKDV, (long)N * DKDV);
+  // this chain's summaries and segment aggregates (single pass), or its runs'
+  // aggregates and inclusive states (runs; nseg runs per chain)
+  const long nU = GR > 1 ? nseg : N;
+  const __amdgpu_buffer_rsrc_t rU = coh_rsrc(Uws + bh * nU * DKDV, nU * DKDV);
   const __amdgpu_buffer_rsrc_t rS = coh_rsrc(Sws + bh * nseg * DKDV, (long)nseg * DKDV);
   if constexpr (kFused) {
-    cw = ctrl + kCtrlHeader + bh * (long)(N + nseg + 1);
+    cw = ctrl + kCtrlHeader + bh * (long)(GR > 1 ? nseg + 1 : N + nseg + 1);
     // -- U_n^T = V^T K^ in 16x16 blocks, staged as rows of key dims (the
     // tile stays in LDS until the segment's aggregate is built), published
     constexpr int NBLK = NE * ND, BPW = (NBLK + 3) / 4;
@@ -300,19 +353,47 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       }
     }
     __syncthreads();
-    // wave 0 alone stores and flags U_n (rows divided by their scales), the
-    // row scales and a_n, so that the other waves go on to their score blocks
-    // without waiting for the stores to complete
-    if (wave == 0) {
-      for (int x8 = 8 * lane; x8 < DKDV; x8 += 8 * 64)
-        st_coh(rU, n * DKDV + x8, *reinterpret_cast<const half8*>(&sU[x8 / DV][x8 % DV]));
-      for (int d = lane; d < DK; d += 64) {
-        const float sg = row_scale(__uint_as_float(sRowMax[d]));
-        sSigU[d] = sg;
-        st_dev2(Aws + 2 * (bhn * DK + d), sAn[d], sg);
+    if constexpr (GR == 1) {
+      // wave 0 alone stores and flags U_n (rows divided by their scales), the
+      // row scales and a_n, so that the other waves go on to their score
+      // blocks without waiting for the stores to complete
+      if (wave == 0) {
+        for (int x8 = 8 * lane; x8 < DKDV; x8 += 8 * 64)
+          st_coh(rU, n * DKDV + x8, *reinterpret_cast<const half8*>(&sU[x8 / DV][x8 % DV]));
+        for (int d = lane; d < DK; d += 64) {
+          const float sg = row_scale(__uint_as_float(sRowMax[d]));
+          sSigU[d] = sg;
+          st_dev2(Aws + 2 * (bhn * DK + d), sAn[d], sg);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0) __hip_atomic_store(cw + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (lane == 0) __hip_atomic_store(cw + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (tid < DK) sSigU[tid] = row_scale(__uint_as_float(sRowMax[tid]));
+      __syncthreads();  // every chunk's U_n, a_n and row scales are in LDS
+      // the run's last chunk publishes the run's aggregate (the state after
+      // the run when it enters at zero, and the run's decay); chunks past the
+      // chain's end are padding (a = 1, U = 0), so every run has GR chunks
+      if (grp == GR - 1 && run > 0) {
+#pragma unroll
+        for (int g = 0; g < NGR; ++g) {
+          const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
+          if (x8 < DKDV) {
+            float x[8], w, m = 0.f;
+            run_prefix(GR, x8, x, w);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(x[c]));
+            // the DV/8 neighbouring lanes of row d agree on its scale
+            const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
+            const float inv = inv_scale(sg);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] *= inv;
+            st_coh(rU, run * DKDV + x8, cvt8(x));
+            if (x8 % DV == 0) st_dev2(Aws + 2 * ((bh * nseg + run) * DK + d), w, sg);
+          }
+        }
+        publish_wave(cw + run, &sPub, kStAgg);
+      }
     }
   }
 
@@ -420,6 +501,22 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     }
   }
 
+  // O_I = sum_{J<=I} A_IJ V_J on the matrix cores (single pass and runs)
+  auto intra_av = [&](floatx4 (&oacc)[NE]) {
+#pragma unroll
+    for (int E = 0; E < NE; ++E) {
+      oacc[E] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (owner) {
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+          if (J <= I) {
+            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
+            oacc[E] = mfma16x16x16(vb, A[J], oacc[E]);
+          }
+        }
+      }
+    }
+  };
   if constexpr (!kFused) {
     __syncthreads();  // K~ is no longer read: its LDS becomes the output tile
     // -- O_I = sum_{J<=I} A_IJ V_J + Q^_I S, with A stored / sigA and the
@@ -456,12 +553,15 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       }
     }
   } else {
+    float xs[NGR][8];  // S_n, by groups of 8 elements of one state row
+    floatx4 oacc[NE];  // the outputs, O_I
+    if constexpr (GR == 1) {
     // -- the entering state, in-segment part: X and W
     const int seg = n / G, n0 = seg * G, nlast = min(n0 + G, N) - 1;
     const bool agg = n == nlast && seg < nseg - 1;  // publishes the segment's aggregate
     if (wave == 0) wave_wait_flags(cw + n0, n - n0, ctrl);
     __syncthreads();
-    float xs[NGR][8], wv[NGR];
+    float wv[NGR];
 #pragma unroll
     for (int g = 0; g < NGR; ++g) {
       wv[g] = 1.f;
@@ -526,20 +626,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     }
     // -- intra-chunk part, while the aggregate's stores complete and the
     // earlier segments publish: O_I = sum_{J<=I} A_IJ V_J
-    floatx4 oacc[NE];
-#pragma unroll
-    for (int E = 0; E < NE; ++E) {
-      oacc[E] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (owner) {
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J <= I) {
-            const half4 vb = ld_tr<VSTR, 4>(&sV[16 * J][16 * E]);
-            oacc[E] = mfma16x16x16(vb, A[J], oacc[E]);
-          }
-        }
-      }
-    }
+    intra_av(oacc);
     if (agg) publish_wave(cw + N + seg, &sPub);
     // -- the state entering the segment, from the earlier segments' aggregates
     if (wave == 0) wave_wait_flags(cw + N, seg, ctrl);
@@ -603,19 +690,125 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
 #pragma unroll
           for (int c = 0; c < 8; ++c) pv[g][c] += w2[g] * z[c];
         }
-        float m = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          xs[g][c] += wv[g] * pv[g][c];  // S_n
-          m = fmaxf(m, fabsf(xs[g][c]));
-        }
+        for (int c = 0; c < 8; ++c) xs[g][c] += wv[g] * pv[g][c];  // S_n
         if (fin) {
           float f[8];
 #pragma unroll
           for (int c = 0; c < 8; ++c) f[c] = sAn[d] * xs[g][c] + sSigU[d] * (float)ul[g][c];
           store_f8(sfin + bh * DKDV + x8, f);
         }
-        // S_n staged in half, row d divided by its scale
+      }
+    }
+    } else {
+      // -- runs: the intra-chunk part first, O_I = sum_{J<=I} A_IJ V_J
+      intra_av(oacc);
+      // -- the state entering the run, S_in: its predecessors' aggregates
+      // folded onto the nearest inclusive state (or the initial state)
+      int nagg = 0, from_start = 1;
+      if (run > 0) {
+        if (threadIdx.x < 64) {
+          int fs;
+          const int na = lookback_runs(cw, run, ctrl, &fs);
+          if (threadIdx.x == 0) sLook[0] = na, sLook[1] = fs;
+        }
+        __syncthreads();
+        nagg = sLook[0], from_start = sLook[1];
+      }
+      float pv[NGR][8], w2[NGR];
+#pragma unroll
+      for (int g = 0; g < NGR; ++g) {
+        w2[g] = 1.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pv[g][c] = 0.f;
+      }
+      for (int j = 0; j < nagg; j += LB) {
+        half8 u[NGR][LB];
+        float a[NGR][LB], su[NGR][LB];
+#pragma unroll
+        for (int g = 0; g < NGR; ++g) {  // clamped, unconditional loads
+          const int x8 = (8 * (tid + kThreads * g)) % DKDV;
+#pragma unroll
+          for (int jj = 0; jj < LB; ++jj) {
+            const int r = run - 1 - min(j + jj, nagg - 1);
+            u[g][jj] = ld_coh(rU, r * DKDV + x8);
+            const float2 pr = ld_dev2(Aws + 2 * ((bh * nseg + r) * DK + x8 / DV));  // (decay, sig)
+            a[g][jj] = pr.x, su[g][jj] = pr.y;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < NGR; ++g) {
+#pragma unroll
+          for (int jj = 0; jj < LB; ++jj) {
+            if (j + jj < nagg) {
+              const float w = w2[g] * su[g][jj];
+#pragma unroll
+              for (int c = 0; c < 8; ++c) pv[g][c] += w * (float)u[g][jj][c];
+              w2[g] *= a[g][jj];
+            }
+            consume(u[g][jj], a[g][jj]);
+            consume(u[g][jj], su[g][jj]);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NGR; ++g) {
+        const int x8 = (8 * (tid + kThreads * g)) % DKDV;
+        if (!from_start) {
+          const int r = run - 1 - nagg;
+          const half8 u = ld_coh(rS, r * DKDV + x8);
+          const float w = w2[g] * ld_dev2(GAws + 2 * ((bh * nseg + r) * DK + x8 / DV)).y;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) pv[g][c] += w * (float)u[c];
+        } else if (s0) {
+          float z[8];
+          load_f8(s0 + bh * DKDV + x8, z);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) pv[g][c] += w2[g] * z[c];
+        }
+      }
+      // -- this chunk's state S_n = X + W S_in, X and W from the run's chunks
+      // before it; the run's last chunk also forms a_n S_n + U_n, the run's
+      // inclusive state (published for the later runs) or the final state
+      const bool last_run = run == nseg - 1;
+#pragma unroll
+      for (int g = 0; g < NGR; ++g) {
+        const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
+        float x[8], w;
+        run_prefix(grp, x8 % DKDV, x, w);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) xs[g][c] = fmaf(w, pv[g][c], x[c]);
+        if (grp == GR - 1 && x8 < DKDV) {
+          const half8 un = *reinterpret_cast<const half8*>(&sU[d][x8 % DV]);
+          float inc[8], m = 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            inc[c] = fmaf(sSigU[d], (float)un[c], sAn[d] * xs[g][c]);
+            m = fmaxf(m, fabsf(inc[c]));
+          }
+          if (last_run) {
+            if (sfin) store_f8(sfin + bh * DKDV + x8, inc);
+          } else {
+            const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
+            const float inv = inv_scale(sg);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) inc[c] *= inv;
+            st_coh(rS, run * DKDV + x8, cvt8(inc));
+            if (x8 % DV == 0) st_dev2(GAws + 2 * ((bh * nseg + run) * DK + d), 1.f, sg);
+          }
+        }
+      }
+      __syncthreads();  // every U tile read: the region becomes S_n's staging tile
+      if (grp == GR - 1 && !last_run) publish_wave(cw + run, &sPub2, kStInc);
+    }
+    // -- S_n staged in half, row d divided by its scale
+#pragma unroll
+    for (int g = 0; g < NGR; ++g) {
+      const int x8 = 8 * (tid + kThreads * g), d = x8 / DV;
+      if (x8 < DKDV) {
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(xs[g][c]));
         const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
         const float inv = inv_scale(sg);
         float o[8];
@@ -697,7 +890,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
     }
     if (sRow[r] >= 0) store8(op + orow * DV + c8, x);
   }
-  if constexpr (kFused) {
+  if constexpr (kFused && GR == 1) {
     // -- this chunk is done reading what its chain published: count it; the
     // last chunk of the chain to finish clears the chain's control words (off
     // the critical path, after the outputs are on their way)
@@ -707,6 +900,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_kernel(
       unsigned* cw = ctrl + kCtrlHeader + bh * (long)(N + nseg + 1);
       for (int i = tid; i < N + nseg + 1; i += kThreads) cw[i] = 0u;
     }
+  } else if constexpr (kFused) {
+    // -- runs: the same per run (status words, then the counter)
+    unsigned* cw = ctrl + kCtrlHeader + bh * (long)(nseg + 1);
+    if (threadIdx.x == 0) sLook[0] = (int)atomicAdd(cw + nseg, 1u);
+    __syncthreads();
+    if (sLook[0] == nseg - 1)
+      for (int i = threadIdx.x; i < nseg + 1; i += kThreads * GR) cw[i] = 0u;
   }
 }
 

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     load_row<DK, NKS>(kp, row, lk, kf);
     load_row<DK, NKS>(gp, row, lk, sc);
   }
-  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV);
+  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV, threadIdx.x);
   if (tid < DK) sRowMax[tid] = 0u;
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
     zero_row<NEL>(pad, kf);

@@ -68,10 +68,10 @@ hipError_t launch_onepass_gated(const Problem& p, int b0, int nb, const DirPack&
                                 const void* q, const void* k, const void* v, const void* gk,
                                 void* o, char* ws, const float* s0, float* sfin,
                                 const Epilogue& epi, hipStream_t s);
-// The forward over runs of kRunChunks chunks per workgroup with a decoupled
-// look-back between runs (gla_runs.hip). Chunk 64 only; requires
-// runs_fit(p, nb).
-constexpr int kRunChunks = 4;
+// The forward over runs of run_chunks(dtype) chunks per workgroup (one group
+// of four waves per chunk) with a decoupled look-back between runs
+// (gla_runs.hip). Chunk 64 only; requires runs_fit(p, nb).
+int run_chunks(int dtype);
 bool runs_fit(const Problem& p, int nb);
 hipError_t launch_runs(const Problem& p, int b0, int nb, const DirPack& dirs, const void* q,
                        const void* k, const void* v, const void* gk, void* o, char* ws,

@@ -40,10 +40,12 @@ __device__ __forceinline__ int token_row(int tok, int T, int gh, int gw, int dir
   return tok < T ? scan_to_raster(tok, T, gh, gw, dir) : -1;
 }
 
-// Raster row of every token of the chunk, for the output scatter.
+// Raster row of every token of the chunk, for the output scatter (tix: the
+// thread's index among the chunk's kThreads threads).
 template <int C>
-__device__ __forceinline__ void chunk_rows(int* sRow, int tok0, int T, int gh, int gw, int dir) {
-  if (threadIdx.x < C) sRow[threadIdx.x] = token_row(tok0 + threadIdx.x, T, gh, gw, dir);
+__device__ __forceinline__ void chunk_rows(int* sRow, int tok0, int T, int gh, int gw, int dir,
+                                           int tix) {
+  if (tix < C) sRow[tix] = token_row(tok0 + tix, T, gh, gw, dir);
 }
 
 // Token row t of a [B][T][H][D] tensor, this lane's 8*NKS dims
@@ -94,23 +96,23 @@ __device__ __forceinline__ half4 ld_tr(const half_t* blk) {
 // V rows of the chunk (scan positions tok0..tok0+C-1) into sV[token][e]
 // (half, zero for padding rows) with 16-byte stores; each thread finds its
 // rows' raster positions itself, and the loads are unconditional as in
-// load_row.
+// load_row (tix: the thread's index among the chunk's kThreads threads).
 template <int DV, int C, int VSTR, typename InT>
 __device__ __forceinline__ void load_v(const InT* vp, int tok0, int T, int gh, int gw, int dir,
-                                       long bT, int H, int h, half_t (*sV)[VSTR]) {
+                                       long bT, int H, int h, half_t (*sV)[VSTR], int tix) {
   constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
   half8 v8[NIT];
   int rows[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int u = threadIdx.x + kThreads * it;
+    const int u = tix + kThreads * it;
     const int r = (u / (DV / 8)) % C, c8 = (u % (DV / 8)) * 8;
     rows[it] = token_row(tok0 + r, T, gh, gw, dir);
     v8[it] = load8h(vp + ((bT + (rows[it] >= 0 ? rows[it] : 0)) * H + h) * DV + c8);
   }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int u = threadIdx.x + kThreads * it;
+    const int u = tix + kThreads * it;
     const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
     if (u < C * (DV / 8)) {
       half8 x = v8[it];
@@ -144,6 +146,9 @@ __device__ __forceinline__ float row_scale(float m) {
   const int e = eb - 140;  // m < 2^(eb-126), so m / 2^e < 2^14
   return (e <= 0 || eb == 255) ? 1.f : __uint_as_float((unsigned)(e + 127) << 23);
 }
+// LDS offsets rounded up to 16 bytes
+constexpr int lds_round(int x) { return (x + 15) & ~15; }
+
 // A value the caller knows to be equal on every lane, made a scalar so that
 // branches on it are scalar branches (the compiler cannot see the equality).
 __device__ __forceinline__ float uniform(float x) {
@@ -285,14 +290,63 @@ __device__ __forceinline__ void wave_wait_flags(const unsigned* flags, int count
   }
 }
 
-// Called once by every wave of the workgroup after it has issued its
-// coherent stores of one publication: the wave waits for their completion
-// and counts itself in *count (LDS, zero beforehand); the last wave to arrive
-// sets the flag. No workgroup barrier, so a wave that arrives early goes on.
-__device__ __forceinline__ void publish_wave(unsigned* flag, unsigned* count) {
+// Called once by every wave of a chunk's kThreads threads after it has
+// issued its coherent stores of one publication: the wave waits for their
+// completion and counts itself in *count (LDS, zero beforehand); the last
+// wave to arrive sets the flag to value. No barrier, so a wave that arrives
+// early goes on.
+__device__ __forceinline__ void publish_wave(unsigned* flag, unsigned* count, unsigned value = 1u) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if ((threadIdx.x & 63) == 0 && atomicAdd(count, 1u) == kThreads / 64 - 1)
-    __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Status words of a chain's runs for the decoupled look-back between runs:
+// 0 nothing yet, kStAgg the run's own aggregate is published, kStInc its
+// inclusive state (everything before it folded in) is.
+constexpr unsigned kStAgg = 1u, kStInc = 2u;
+
+// Called by one wave for run `run` > 0 of a chain whose status words are
+// st[0..]: waits until some predecessor p has kStInc with every run between
+// p and `run` at least kStAgg, or every predecessor down to the chain's start
+// is at least kStAgg. Returns the number of aggregates to fold in (the runs
+// run-1 down to p+1, or all of them) and sets *from_start when the chain's
+// start (the initial state) takes the place of an inclusive state. Windows
+// of 64 predecessors, one lane each; every wait is bounded (running out sets
+// the sticky error bit in *err and returns with results invalid).
+__device__ __forceinline__ int lookback_runs(const unsigned* st, int run, unsigned* err,
+                                            int* from_start) {
+  const int lane = threadIdx.x & 63;
+  for (int j0 = 0;; j0 += 64) {
+    const int cnt = min(64, run - j0);  // predecessors run-1-j0-lane, lane < cnt
+    for (long it = 0;; ++it) {
+      unsigned v = 0u;
+      if (lane < cnt)
+        v = __hip_atomic_load(st + (run - 1 - j0 - lane), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long inc = __ballot(lane < cnt && v == kStInc);
+      const unsigned long long none = __ballot(lane < cnt && v == 0u);
+      if (inc) {
+        const int jl = __builtin_ctzll(inc);
+        if ((none & ((1ull << jl) - 1ull)) == 0ull) {
+          *from_start = 0;
+          return j0 + jl;
+        }
+      } else if (none == 0ull) {
+        if (j0 + cnt == run) {  // every predecessor aggregated: start from the initial state
+          *from_start = 1;
+          return run;
+        }
+        break;  // all aggregated: the next window
+      }
+      if (it >= kSpinLimit) {
+        if (lane == 0) atomicOr(err, kErrSpin);
+        *from_start = 1;
+        return j0 + cnt;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
 }
 
 }  // namespace tile

@@ -1,5 +1,6 @@
-"""GPU parity of the runs schedule (one workgroup per run of four 64-token
-chunks, decoupled look-back between runs) against the float64 oracle.
+"""GPU parity of the runs schedule (one workgroup per run of 64-token chunks,
+four for half inputs and three for float, one group of four waves per chunk;
+decoupled look-back between runs) against the float64 oracle.
 
 Bar: max|x - x_ref| / max|x_ref| <= 5e-3 for outputs and final states.
 """
