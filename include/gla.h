@@ -151,17 +151,21 @@ size_t gla_fwd_workspace_bytes(int B, int H, int grid_h, int grid_w, int dk,
 
 /* Byte offsets, within the workspace, of the intermediate arrays, so that
  * callers (tests) can inspect them after the phase calls below:
- *   U : half  [B][H][N][dk][dv]   chunk summaries (both schedules), row d
- *                                 stored divided by its scale sigU
- *   a : float [B][H][N][dk][2]    pairs (a_n[d], sigU_n[d]): the per-chunk
- *                                 total decay exp(sum of gk) and the scale
- *                                 of U_n row d
- *   S : half  [B][H][N][dk][dv]   state entering each chunk (three phases;
- *                                 the single pass keeps segment aggregates),
- *                                 row d stored divided by its scale sigS
+ *   U : half  [B][H][N][dk][dv]   chunk summaries, row d stored divided by
+ *                                 its scale sigU_n[d] = row_scale(m_n[d])
+ *   a : float [B][H][N][dk][2]    pairs (a_n[d], m_n[d]): the per-chunk
+ *                                 total decay exp(sum of gk) and the largest
+ *                                 |U_n[d][e]| over e (before scaling)
+ *   S : half  [B][H][N][dk][dv]   state entering each chunk, row d stored
+ *                                 divided by its scale sigS_n[d]
  *   scales : float [B][H][N][dk]  sigS_n[d], at off_scales
- * Scales are exact powers of two >= 1 (1 unless the row's magnitude passes
- * 2^14); the stored row times its scale is the value. N = ceil(T / chunk).
+ * row_scale(m) is 1 for m < 2^14 and otherwise the power of two 2^e that
+ * brings m / 2^e into [2^13, 2^14); the stored row times its scale is the
+ * value. These are the three phases' arrays, as gla_chunk_summaries and
+ * gla_state_scan leave them; the single-pass and runs schedules reuse the
+ * same regions for their own publications (summaries with the pairs
+ * (a_n[d], sigU_n[d]), segment or run aggregates and inclusive states), which
+ * are not meant to be read. N = ceil(T / chunk).
  * Returns GLA_OK or GLA_E_ARG/GLA_E_UNSUPPORTED. */
 int gla_workspace_layout(int B, int H, int grid_h, int grid_w, int dk, int dv,
                          int chunk, size_t* off_U, size_t* off_a,

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   constexpr int L_AN = L_F + (kFused ? NB : 1) * DK * 4, L_ROW = L_AN + (kFused ? DK : 1) * 4;
   constexpr int L_SIG = L_ROW + C * 4, L_RMAX = L_SIG + DK * 4;
   constexpr int L_SIGU = L_RMAX + (kFused ? DK : 1) * 4, L_W = L_SIGU + (kFused ? DK : 1) * 4;
-  constexpr int PER = lds_round(L_W + 16);
+  constexpr int PER = lds_round(L_W + 20);
   static_assert(GR * PER <= 160 * 1024, "the chunks of a workgroup exceed the LDS of a CU");
   __shared__ __attribute__((aligned(16))) char sL[GR * PER];
   __shared__ int sLook[2];  // runs: the look-back's result, for the whole workgroup
@@ -117,6 +117,11 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   unsigned& sDone = *reinterpret_cast<unsigned*>(lb + L_W + 4);
   unsigned& sPub = *reinterpret_cast<unsigned*>(lb + L_W + 8);
   unsigned& sPub2 = *reinterpret_cast<unsigned*>(lb + L_W + 12);
+  // single pass and runs: the largest row scale of S_n as float bits (it
+  // shares sSigMax's word), and whether any entry of U_n reached the half
+  // range; both are rare, so their common case costs one wave vote each
+  unsigned& sSigMaxBits = *reinterpret_cast<unsigned*>(lb + L_W);
+  unsigned& sBigU = *reinterpret_cast<unsigned*>(lb + L_W + 16);
   half_t (*sKt)[KSTR] = reinterpret_cast<half_t (*)[KSTR]>(sKO);
   InT (*sO)[OSTR] = reinterpret_cast<InT (*)[OSTR]>(sKO);
   // The outputs are produced transposed (O^T = V^T A^T + S^T Q^T: the same
@@ -181,6 +186,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   // the barrier that follows the cumulative sums
   chunk_rows<C>(sRow, n * C, T, gh, gw, dir, tid);
   if (tid == 0) sPub = 0u, sPub2 = 0u;
+  if (kFused && tid == 0) sSigMaxBits = 0x3f800000u, sBigU = 0u;  // 1.0f; none
   if (kFused && tid < DK) sRowMax[tid] = 0u;
 
   // -- this wave's token rows of q, k, gk in the operand layout (waves past
@@ -324,10 +330,12 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     // tile stays in LDS until the segment's aggregate is built), published
     constexpr int NBLK = NE * ND, BPW = (NBLK + 3) / 4;
     floatx4 uacc[BPW];
+    float um[BPW];  // this lane's largest |entry| of each block
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int blk = wave + 4 * i;
       uacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      um[i] = 0.f;
       if (blk < NBLK) {
         const int E = blk / ND, D = blk % ND;
 #pragma unroll
@@ -336,19 +344,33 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
           const half4 bb = ld_tr<HSTR, 4>(&sKh[16 * J][16 * D]);
           uacc[i] = mfma16x16x16(a, bb, uacc[i]);
         }
-        const float m = fmaxf(fmaxf(fabsf(uacc[i][0]), fabsf(uacc[i][1])),
-                              fmaxf(fabsf(uacc[i][2]), fabsf(uacc[i][3])));
-        atomicMax(&sRowMax[16 * D + lr], __float_as_uint(m));
+        um[i] = fmaxf(fmaxf(fabsf(uacc[i][0]), fabsf(uacc[i][1])),
+                      fmaxf(fabsf(uacc[i][2]), fabsf(uacc[i][3])));
       }
     }
+    // row maxima only from waves with an entry of 2^14 or more: a row whose
+    // maximum is below that has scale 1 whatever is posted, and a row whose
+    // maximum is not gets that maximum from the wave holding it
+    float uw = 0.f;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) uw = fmaxf(uw, um[i]);
+    if (__any(uw >= kRowRange)) {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int blk = wave + 4 * i;
+        if (blk < NBLK) atomicMax(&sRowMax[16 * (blk % ND) + lr], __float_as_uint(um[i]));
+      }
+      if (lane == 0) sBigU = 1u;
+    }
     __syncthreads();  // K^ is no longer read: the region becomes the U staging tile
+    const bool scale_u = sBigU != 0u;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int blk = wave + 4 * i;
       if (blk < NBLK) {
         const int E = blk / ND, D = blk % ND;
-        const float inv = inv_scale(row_scale(__uint_as_float(sRowMax[16 * D + lr])));
-        const floatx4 x = uacc[i] * inv;
+        floatx4 x = uacc[i];
+        if (scale_u) x *= inv_scale(row_scale(__uint_as_float(sRowMax[16 * D + lr])));
         *reinterpret_cast<half4*>(&sU[16 * D + lr][16 * E + 4 * lq]) = cvt4(x);
       }
     }
@@ -361,7 +383,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
         for (int x8 = 8 * lane; x8 < DKDV; x8 += 8 * 64)
           st_coh(rU, n * DKDV + x8, *reinterpret_cast<const half8*>(&sU[x8 / DV][x8 % DV]));
         for (int d = lane; d < DK; d += 64) {
-          const float sg = row_scale(__uint_as_float(sRowMax[d]));
+          const float sg = scale_u ? row_scale(__uint_as_float(sRowMax[d])) : 1.f;
           sSigU[d] = sg;
           st_dev2(Aws + 2 * (bhn * DK + d), sAn[d], sg);
         }
@@ -369,7 +391,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
         if (lane == 0) __hip_atomic_store(cw + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
-      if (tid < DK) sSigU[tid] = row_scale(__uint_as_float(sRowMax[tid]));
+      if (tid < DK) sSigU[tid] = scale_u ? row_scale(__uint_as_float(sRowMax[tid])) : 1.f;
       __syncthreads();  // every chunk's U_n, a_n and row scales are in LDS
       // the run's last chunk publishes the run's aggregate (the state after
       // the run when it enters at zero, and the run's decay); chunks past the
@@ -614,10 +636,13 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
             m = fmaxf(m, fabsf(ag[c]));
           }
           // the DV/8 neighbouring lanes of row d agree on its scale
-          const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
-          const float inv = inv_scale(sg);
+          float sg = 1.f;
+          if (__any(m >= kRowRange)) {
+            sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
+            const float inv = inv_scale(sg);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) ag[c] *= inv;
+            for (int c = 0; c < 8; ++c) ag[c] *= inv;
+          }
           st_coh(rS, seg * DKDV + x8, cvt8(ag));
           // with the segment's decay: the weight the look-back accumulated, times a_n
           if (x8 % DV == 0) st_dev2(GAws + 2 * (gs * DK + d), wv[g] * sAn[d], sg);
@@ -809,11 +834,16 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
         float m = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(xs[g][c]));
-        const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
-        const float inv = inv_scale(sg);
-        float o[8];
+        float o[8], sg = 1.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = xs[g][c] * inv;
+        for (int c = 0; c < 8; ++c) o[c] = xs[g][c];
+        if (__any(m >= kRowRange)) {
+          sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
+          const float inv = inv_scale(sg);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[c] *= inv;
+          if (sg != 1.f) atomicMax(&sSigMaxBits, __float_as_uint(sg));  // positive floats
+        }
         *reinterpret_cast<half8*>(&sS[d][x8 % DV]) = cvt8(o);
         if (x8 % DV == 0) sSig[d] = sg;
       }
@@ -823,8 +853,8 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     // row scales of S_n folded into Q^ (factors sigS[d] / max sigS <= 1) and
     // the accumulators taken / max sigS meanwhile
     if (owner) {
-      // the largest row scale, by a reduction within the wave
-      const float smax = uniform(group_max<64>(sSig[lane % DK]));
+      // the largest row scale (1 unless some row was scaled)
+      const float smax = uniform(__uint_as_float(sSigMaxBits));
       if (smax != 1.f) {
         const float is = inv_scale(smax);
 #pragma unroll

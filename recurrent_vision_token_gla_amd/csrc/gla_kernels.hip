@@ -284,7 +284,16 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
     store_f8(sfin + bh * DKDV + x8, f);
   }
   // -- replay the segment from its entering state; a segment longer than one
-  // register block reads its chunks again (the registers hold the last block)
+  // register block reads its chunks again (the registers hold the last
+  // block). The state is kept divided by its current row scale 2^es, which
+  // the update folds in (exact power-of-two factors), so each stored row is
+  // a plain conversion.
+  int es = row_scale_exp(M);
+  {
+    const float inv = __builtin_amdgcn_ldexpf(1.f, -es);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] *= inv;
+  }
   const bool cached = n1 - n0 <= kScanRegs;
   for (int nb = n0; nb < n1; nb += kScanRegs) {
     if (!cached) {
@@ -298,17 +307,21 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
 #pragma unroll
     for (int i = 0; i < kScanRegs; ++i) {
       if (nb + i < n1) {
-        const int es = row_scale_exp(M);
-        const float inv = __builtin_amdgcn_ldexpf(1.f, -es);
         half8 o;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = (half_t)(s[c] * inv);
+        for (int c = 0; c < 8; ++c) o[c] = (half_t)s[c];
         *reinterpret_cast<half8*>(S + (long)(nb + i) * DKDV) = o;
         if (row_lead) SS[(long)(nb + i) * DK] = __builtin_amdgcn_ldexpf(1.f, es);
-        const float su = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(ac[i].y));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s[c] = fmaf((float)uc[i][c], su, ac[i].x * s[c]);
         M = ac[i].x * M + ac[i].y;
+        const int en = row_scale_exp(M);
+        // s <- (a s + sigU u) / 2^en, with s held / 2^es (the factors are
+        // powers of two, so this is exact scaling of the unscaled update; no
+        // branch: one on loaded data would wait for every load in flight)
+        const float f = __builtin_amdgcn_ldexpf(ac[i].x, es - en);
+        const float g = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(ac[i].y) - en);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = fmaf((float)uc[i][c], g, f * s[c]);
+        es = en;
       }
     }
   }
@@ -356,30 +369,43 @@ __global__ __launch_bounds__(kThreads) void scan_serial_kernel(
     u[i] = *reinterpret_cast<const half8*>(U + m * DKDV);
     a[i] = A[m * DK];
   }
+  // the state is kept divided by its current row scale 2^es (as in scan_kernel)
+  int es = row_scale_exp(M);
+  {
+    const float inv = __builtin_amdgcn_ldexpf(1.f, -es);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] *= inv;
+  }
   for (int n0 = 0; n0 < N; n0 += W) {
 #pragma unroll
     for (int i = 0; i < W; ++i) {
       const int n = n0 + i;
       if (n < N) {
         // the state entering chunk n
-        const int es = row_scale_exp(M);
-        const float inv = __builtin_amdgcn_ldexpf(1.f, -es);
         half8 o;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = (half_t)(s[c] * inv);
+        for (int c = 0; c < 8; ++c) o[c] = (half_t)s[c];
         *reinterpret_cast<half8*>(S + n * DKDV) = o;
         if (row_lead) SS[(long)n * DK] = __builtin_amdgcn_ldexpf(1.f, es);
-        const float su = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(a[i].y));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s[c] = fmaf((float)u[i][c], su, a[i].x * s[c]);
         M = a[i].x * M + a[i].y;
+        const int en = row_scale_exp(M);
+        const float f = __builtin_amdgcn_ldexpf(a[i].x, es - en);
+        const float g = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(a[i].y) - en);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = fmaf((float)u[i][c], g, f * s[c]);
+        es = en;
       }
       const long m = n + W < N ? n + W : N - 1;  // refill the slot (clamped)
       u[i] = *reinterpret_cast<const half8*>(U + m * DKDV);
       a[i] = A[m * DK];
     }
   }
-  if (sfin) store_f8(sfin + bh * DKDV + x8, s);
+  if (sfin) {
+    const float sc = __builtin_amdgcn_ldexpf(1.f, es);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] *= sc;
+    store_f8(sfin + bh * DKDV + x8, s);
+  }
 }
 
 __global__ void scan_perm_kernel(int32_t* perm, int T, int gh, int gw, int dir) {
