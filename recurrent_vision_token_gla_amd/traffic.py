@@ -32,9 +32,13 @@ def kernel_class(name: str) -> str | None:
     if "copyBuffer" in name:
         return "copy"
     if "chunk_kernel" in name:
-        # template arguments <DK, DV, C, InT, kFused, kGate>: the two flags
-        # mangle as Lb<0|1>ELb<0|1>E, demangled as "true, ..." / "false, ..."
-        m = re.search(r"Lb([01])ELb([01])E", name) or re.search(r"(true|false), (true|false)>", name)
+        # template arguments <DK, DV, C, InT, kFused, kGate, GR>: the flags
+        # mangle as Lb<0|1>ELb<0|1>E and GR (chunks per workgroup) as Li<GR>E;
+        # demangled, "true, false, 4>"
+        m = (re.search(r"Lb([01])ELb([01])ELi(\d+)E", name)
+             or re.search(r"(true|false), (true|false), (\d+)>", name))
+        if m and int(m.group(3)) > 1:
+            return "runs"
         return "single_pass" if m and m.group(1) in ("1", "true") else "outputs"
     if "summary_kernel" in name:
         return "summaries"
