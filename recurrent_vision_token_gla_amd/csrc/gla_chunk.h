@@ -30,9 +30,9 @@ namespace tile {
 //                       K' = k 2^(s_7 - s_j): one reference at the 8th token.
 // Each wave picks the diagonal block's arithmetic from its own 16 tokens:
 // half operands while no key dim decays by more than 2^8 over the block and
-// max(|q|, |k|) * 2^range stays within 2^15, float operands while the range
+// max(|Q~|, |K~|) * 2^range stays within 2^15, float operands while the range
 // is within 2^120 and those factors stay finite, and beyond that a direct
-// float sum of every entry from 2^(s_i - s_j). Score entries beyond 2^14 in
+// float sum of every entry from 2^(s_i - s_j) (q and k read again). Score entries beyond 2^14 in
 // magnitude make the wave divide its score blocks by a power of two sigA,
 // undone on the accumulators (the product with V is linear).
 //
@@ -193,15 +193,16 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   // the last sub-block load a padding row too: no branch around the loads)
   const bool owner = wave < NB;
   const int I = wave, t = 16 * I + lr;
-  float qf[NEL], kf[NEL], sc[NEL];
+  RawRow<InT, NKS> qr, kr, gr;  // as loaded, converted where consumed
+  float sc[NEL];
   bool pad;  // this lane's token row is padding
   {
     const int rr = owner ? token_row(n * C + t, T, gh, gw, dir) : -1;
     const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
     pad = row < 0;
-    load_row<DK, NKS>(qp, row, lk, qf);
-    load_row<DK, NKS>(kp, row, lk, kf);
-    load_row<DK, NKS>(gp, row, lk, sc);
+    qr.load(qp, row, DK, lk);
+    kr.load(kp, row, DK, lk);
+    gr.load(gp, row, DK, lk);
   }
   // -- the entering state (stored [dk][dv], staged as rows sS[d][e]; three-
   // phase schedule only) and the chunk's V rows, through LDS; every load is
@@ -229,14 +230,14 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   }
 
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
-    zero_row<NEL>(pad, qf);
-    zero_row<NEL>(pad, kf);
-    zero_row<NEL>(pad, sc);
+    qr.zero_if(pad);
+    kr.zero_if(pad);
+    gr.zero_if(pad);
   }
-  // -- in-sub-block inclusive cumsum along tokens (DPP row scan)
+  // -- in-sub-block inclusive cumsum along tokens (DPP row scan), in log2
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]) * kLog2e;
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(gr[e] * kLog2e);
     if (lr == 15 || lr == 7) {
 #pragma unroll
       for (int e = 0; e < NEL; ++e) {
@@ -290,25 +291,23 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   // -- per-element factors; K~ goes to LDS for the other sub-blocks, and in
   // one pass K^ = K~ 2^(totals of the later sub-blocks), for U
   float qt[NEL], kt[NEL];
-  float rng = 0.f, big = 0.f;  // this lane's decay range (log2) and max(|q|, |k|)
+  // this lane's decay range over its sub-block (log2) and max(|Q~|, |K~|)
+  float rng = 0.f, bigt = 0.f;
   if (owner) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       float tt[8], ff[8];
       lds8(&sTot[I][32 * ks + lk], tt);
 #pragma unroll
-      for (int c = 0; c < 8; c += 2) {
-        rng = max3f(rng, -tt[c], -tt[c + 1]);
-        big = max3f(big, fabsf(qf[8 * ks + c]), fabsf(kf[8 * ks + c]));
-        big = max3f(big, fabsf(qf[8 * ks + c + 1]), fabsf(kf[8 * ks + c + 1]));
-      }
+      for (int c = 0; c < 8; c += 2) rng = max3f(rng, -tt[c], -tt[c + 1]);
       if constexpr (kFused) lds8(&sF[I][32 * ks + lk], ff);
       half8 k8, kh8;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int e = 8 * ks + c;
-        qt[e] = qf[e] * fexp2(sc[e]);
-        kt[e] = kf[e] * fexp2(tt[c] - sc[e]);
+        qt[e] = qr[e] * fexp2(sc[e]);
+        kt[e] = kr[e] * fexp2(tt[c] - sc[e]);
+        bigt = max3f(bigt, fabsf(qt[e]), fabsf(kt[e]));
         k8[c] = (half_t)kt[e];
         if constexpr (kFused) kh8[c] = (half_t)(kt[e] * ff[c]);
       }
@@ -423,9 +422,10 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   half8 qh[NKS];
   float sigA = 1.f;  // this wave's score blocks are stored divided by sigA
   if (owner) {
-    // the diagonal operands are q 2^(s_i - s_7) and k 2^(s_7 - s_j), each
-    // at most max(|q|, |k|) 2^range in magnitude
-    const float amp = big * fexp2(fminf(rng, 127.f));
+    // the diagonal operands are Q~ 2^(-s_7) = q 2^(s_i - s_7) and
+    // K~ 2^(s_7 - tot) = k 2^(s_7 - s_j), each at most max(|Q~|, |K~|)
+    // 2^range in magnitude
+    const float amp = bigt * fexp2(fminf(rng, 127.f));
     const int tier = __all(rng <= kHalfRange && amp <= 32768.f)  ? 0
                      : __all(rng <= kF32Range && amp < 0x1p126f) ? 1
                                                                   : 2;
@@ -434,16 +434,15 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     if (tier == 0) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        float r1[8], r2[8];
+        float r1[8], r2[8], qa[8], ka[8];
         lds8(&sR1[I][32 * ks + lk], r1);
         lds8(&sR2[I][32 * ks + lk], r2);
-        half8 qa, ka;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          qa[c] = (half_t)(qt[8 * ks + c] * r1[c]);
-          ka[c] = (half_t)(kt[8 * ks + c] * r2[c]);
+          qa[c] = qt[8 * ks + c] * r1[c];
+          ka[c] = kt[8 * ks + c] * r2[c];
         }
-        dacc = mfma16x16x32(ka, qa, dacc);
+        dacc = mfma16x16x32(cvt8(ka), cvt8(qa), dacc);
       }
     } else if (tier == 1) {
 #pragma unroll
@@ -457,19 +456,39 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
                                                       dacc, 0, 0, 0);
       }
     } else {
-      // every entry directly: A_ij = sum_d q_i k_j 2^(s_i - s_j)
+      // every entry directly: A_ij = sum_d q_i k_j 2^(s_i - s_j), with this
+      // lane's q and k rows read again, eight dims at a time (keeping them
+      // in registers through the common tiers would cost more than this
+      // rare reload)
+      const int rr = token_row(n * C + t, T, gh, gw, dir);
+      const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
+      float part[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) part[j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        RawRow<InT, 1> q2, k2;
+        q2.load(qp + 32 * ks, row, DK, lk);
+        k2.load(kp + 32 * ks, row, DK, lk);
+        q2.zero_if(row < 0);
+        k2.zero_if(row < 0);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float qv = q2[c], kv = k2[c], sv = sc[8 * ks + c];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float kj = __shfl(kv, (lane & 48) | j);
+            const float sj = __shfl(sv, (lane & 48) | j);
+            part[j] += qv * kj * fexp2(sv - sj);
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < NEL; ++e) {
-          const float kj = __shfl(kf[e], (lane & 48) | j);
-          const float sj = __shfl(sc[e], (lane & 48) | j);
-          part += qf[e] * kj * fexp2(sc[e] - sj);
-        }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        if ((j >> 2) == lq) dacc[j & 3] = part;
+        float pj = part[j];
+        pj += __shfl_xor(pj, 16);
+        pj += __shfl_xor(pj, 32);
+        if ((j >> 2) == lq) dacc[j & 3] = pj;
       }
     }
     floatx4 Af[NB];  // score blocks in float, before the cast to half

@@ -72,24 +72,25 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
 
   const bool owner = wave < NB;
   const int I = wave, t = 16 * I + lr;
-  float kf[NEL], sc[NEL];
+  RawRow<InT, NKS> kr, gr;  // as loaded, converted where consumed
+  float sc[NEL];
   bool pad;  // this lane's token row is padding
   {
     const int rr = owner ? token_row(n * C + t, T, gh, gw, dir) : -1;
     const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
     pad = row < 0;
-    load_row<DK, NKS>(kp, row, lk, kf);
-    load_row<DK, NKS>(gp, row, lk, sc);
+    kr.load(kp, row, DK, lk);
+    gr.load(gp, row, DK, lk);
   }
   load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV, threadIdx.x);
   if (tid < DK) sRowMax[tid] = 0u;
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
-    zero_row<NEL>(pad, kf);
-    zero_row<NEL>(pad, sc);
+    kr.zero_if(pad);
+    gr.zero_if(pad);
   }
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(sc[e]) * kLog2e;
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(gr[e] * kLog2e);
     if (lr == 15) {
 #pragma unroll
       for (int e = 0; e < NEL; ++e) sTot[I][32 * (e / 8) + lk + (e % 8)] = sc[e];
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
       half8 kh8;
 #pragma unroll
       for (int c = 0; c < 8; ++c)  // B - b_t: the decay of the later tokens
-        kh8[c] = (half_t)(kf[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
+        kh8[c] = (half_t)(kr[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
       *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = kh8;
     }
   }

@@ -67,6 +67,35 @@ __device__ __forceinline__ void load_row(const InT* p, long row, int lk, float* 
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[8 * ks + c] = y[ks][c];
 }
+// The same row kept as loaded (half rows in their 16-byte vectors), converted
+// where each element is consumed: a conversion then folds into the product
+// that uses it (v_fma_mix) instead of taking an instruction of its own.
+template <typename InT, int NKS> struct RawRow;
+template <int NKS> struct RawRow<half_t, NKS> {
+  half8 v[NKS];
+  __device__ __forceinline__ void load(const half_t* p, long row, int D, int lk) {
+    const half_t* r = p + (row >= 0 ? row : 0) * D + lk;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) v[ks] = *reinterpret_cast<const half8*>(r + 32 * ks);
+  }
+  __device__ __forceinline__ void zero_if(bool pad) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) v[ks] = pad ? half8{} : v[ks];
+  }
+  __device__ __forceinline__ float operator[](int e) const { return (float)v[e / 8][e % 8]; }
+};
+template <int NKS> struct RawRow<float, NKS> {
+  float x[8 * NKS];
+  __device__ __forceinline__ void load(const float* p, long row, int D, int lk) {
+    load_row<0, NKS>(p + (row >= 0 ? row : 0) * D, 0, lk, x);
+  }
+  __device__ __forceinline__ void zero_if(bool pad) {
+#pragma unroll
+    for (int e = 0; e < 8 * NKS; ++e) x[e] = pad ? 0.f : x[e];
+  }
+  __device__ __forceinline__ float operator[](int e) const { return x[e]; }
+};
+
 template <int NEL>
 __device__ __forceinline__ void zero_row(bool pad, float* x) {
 #pragma unroll
