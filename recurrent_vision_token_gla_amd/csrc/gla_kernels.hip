@@ -4,16 +4,17 @@
 // summary of GTR, "Methodology in Plain English"): per-chunk summaries in
 // parallel over the chunk x head grid, a light scan of the chunk-boundary
 // states along the chunk axis, then every chunk's outputs in parallel with the
-// causal intra-chunk tile held on chip (LDS) and the boundary-state readout
-// fused in. All three phases read their tokens through the scan-order index
+// causal intra-chunk tile held on chip (in registers) and the boundary-state
+// readout fused in. All three phases read their tokens through the scan-order index
 // math, so no permuted copy of any tensor is ever made.
 //
 // Notation inside a chunk of C tokens (local index i), per key dim d, with
 // g2 = gk * log2(e) so that every exponential is a base-2 exp2:
 //   b_i = sum_{r<=i} g2_r                 inclusive cumulative log2-decay
 //   B   = b_{C-1}                          (padding tokens have g2 = 0)
-// Every factor fed to a half-precision matrix product is <= 1 in magnitude
-// (times |q| or |k|), so strong decay cannot overflow it:
+// Every decay factor fed to a half-precision matrix product off the score
+// tile's diagonal is <= 1 in magnitude (times |q| or |k|), so strong decay
+// cannot overflow it:
 //   summary : K^[j] = k_j * 2^(B - b_j)
 //   readout : Q^[i] = q_i * 2^(b_i)
 //   off-diagonal 16x16 sub-blocks (I > J) of the score tile:
@@ -21,8 +22,12 @@
 //       m_IJ  = 2^(beta_I - e_J)
 //     with beta_I = b at the token before sub-block I and e_J = b at the
 //     last token of sub-block J; A_IJ = (Q~_I * m_IJ) K~_J^T.
-//   diagonal sub-blocks are exact for any gk <= 0: running products of the
-//     per-token decays 2^(g2), never a ratio of two exponentials.
+//   diagonal sub-blocks: one reference at the sub-block's 8th token,
+//     q_i 2^(b_i - b_7) and k_j 2^(b_7 - b_j), factors up to 2^range; each
+//     wave picks half operands, float operands or a direct sum of every entry
+//     from the range and the operands' magnitude (chunk_kernel).
+// Stored states (U, S, aggregates) are half rows divided by power-of-two
+// row scales (row_scale in gla_tile.h), so any state fp32 holds fits.
 #include "gla_launch.h"
 
 #include "gla_chunk.h"
