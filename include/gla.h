@@ -57,8 +57,8 @@
  * publishes it, computes its intra-chunk part, then takes its entering state
  * from the summaries its predecessors publish (grouped in about sqrt(N)
  * segments, whose last chunks publish segment aggregates), and adds the
- * readout. Workgroups run in chain-major order and only wait on earlier
- * ones, with bounded waits. gla_fwd_schedule and gla_auto_schedule say which
+ * readout. Workgroups run in chunk-major order (chunk n of every chain,
+ * then chunk n + 1) and only wait on earlier ones, with bounded waits. gla_fwd_schedule and gla_auto_schedule say which
  * one a call takes.
  *
  * Workspace: caller-owned device memory of gla_fwd_workspace_bytes bytes,

@@ -92,16 +92,18 @@ int check_tensor(const void* t) { return (t && aligned(t, 16)) ? GLA_OK : GLA_E_
 
 // Auto dispatch: the single pass saves two kernel boundaries and one read of
 // k, v, gk, but every chunk reads O(sqrt(N)) published tiles. Measured on
-// MI355X (64/64, chunk 64, graph-replayed), single pass against three phases:
-// chains of 25 chunks 12.9 vs 14.1 us at 150 chunk-heads, 45.9 vs 47.5 at
-// 2,400 and 221.9 vs 229.5 at 12,288, but 84.5 vs 82.8 at 4,800 and 115.9 vs
-// 103.6 at 6,144; chains of 49 chunks 16.9 vs 18.4 at 294 chunk-heads and
-// behind from about 2,400; chains of 64 chunks 20.1 vs 18.9 at 384. Chains
-// of 26 to 32 and 50 to 56 chunks were not measured: the limits below
-// interpolate between those points.
-constexpr int kOnepassAnyGrid = 32;      // chains this short: single pass at any grid
-constexpr int kOnepassMaxChain = 56;     // up to here: on small grids only
-constexpr long kOnepassMaxChunks = 512;  // chunk-heads of such a small grid
+// MI355X (64/64, chunk 64, graph-replayed over rotating inputs), single pass
+// against three phases, in us per call: chains of 25 chunks 13.5 vs 16.2 at
+// 150 chunk-heads, 47.7 vs 55.5 at 2,400, 166 vs 188 at 9,600; chains of 49
+// chunks 16.9 vs 20.7 at 294, 160 vs 186 at 9,408; chains of 64 chunks 19.3
+// vs 21.8 at 384, 116 vs 122 at 6,144; chains of 100 chunks 26.6 vs 25.8 at
+// 600, 65.6 vs 58.0 at 2,400, 128 vs 122 at 6,400, 240 vs 243 at 12,800;
+// chains of 144 chunks 39.0 vs 34.9 at 864, 183 vs 197 at 9,216; chains of
+// 256 chunks 60.8 vs 45.8 at 1,536. Long chains favour the single pass only
+// on large grids, about where chunk-heads x N reaches 1.2e6.
+constexpr int kOnepassAnyGrid = 64;         // chains this short: single pass at any grid
+constexpr int kOnepassMaxChain = 144;       // longest chain measured to gain on large grids
+constexpr long kOnepassLongWork = 1200000;  // chunk-heads x N from which those gain
 
 bool single_pass_fits(const gla::Problem& p) {
   const int nb_max = p.B < gla::kMaxBatchPerLaunch ? p.B : gla::kMaxBatchPerLaunch;
@@ -110,7 +112,7 @@ bool single_pass_fits(const gla::Problem& p) {
 
 bool prefer_single_pass(const gla::Problem& p) {
   return p.N <= kOnepassAnyGrid ||
-         (p.N <= kOnepassMaxChain && (long)p.B * p.H * p.N <= kOnepassMaxChunks);
+         (p.N <= kOnepassMaxChain && (long)p.B * p.H * p.N * p.N >= kOnepassLongWork);
 }
 
 int outputs_impl(const void* q, const void* k, const void* v, const void* gk, void* o, int B,

@@ -42,9 +42,11 @@ namespace tile {
 //
 // kFused = false: phase 3 of three; S_n comes from the boundary scan.
 // kFused = true: the whole forward in one pass (the chunk summary, the
-// boundary state and the outputs). Workgroups run in chain-major order, so a
-// chunk only ever waits on chunks of lower index, which were dispatched
-// earlier. Each chunk
+// boundary state and the outputs). Workgroups are numbered chunk-major (chunk
+// n of every chain, then chunk n + 1), so a chunk only ever waits on chunks
+// of lower index, which were dispatched earlier, and the workgroups resident
+// at any time are the earliest unfinished chunks of every chain rather than
+// whole chains waiting on one another's publications. Each chunk
 //   1. computes its summary U_n and decay a_n and publishes them;
 //   2. takes the state it enters, in two levels over segments of G chunks:
 //        S_n = X + W (.) P,  X = sum_{s0 <= m < n} (prod_{m<j<n} a_j) (.) U_m,
@@ -172,8 +174,11 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     const int ch = blockIdx.x - run * nch;
     n = run * GR + grp, h = ch % H, b = ch / H;
   } else if constexpr (kFused) {
-    const int bh = blockIdx.x / N;
-    n = blockIdx.x - bh * N, h = bh % H, b = bh / H;
+    // chunk-major: chunk n of every chain, then chunk n + 1
+    const int nbh = (int)(gridDim.x / N);
+    n = blockIdx.x / nbh;
+    const int bh = blockIdx.x - n * nbh;
+    h = bh % H, b = bh / H;
   } else {
     n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   }
@@ -990,7 +995,7 @@ hipError_t onepass_t(const Problem& p, int b0, int nb, const DirPack& dirs, cons
   const long bhn = (long)b0 * p.H * p.N;
   const long bhs = (long)b0 * p.H * sg.nseg;
   const long st = (long)b0 * p.H * DK * DV;
-  // chain-major: every chunk of one (batch, head) before the next chain
+  // chunk-major: chunk n of every (batch, head) chain before chunk n + 1
   dim3 grid((unsigned)((long)nb * p.H * p.N));
   hipLaunchKernelGGL((chunk_kernel<DK, DV, C, InT, true, kGate>), grid, dim3(kThreads), 0, s,
                      static_cast<const InT*>(q) + tok * DK, static_cast<const InT*>(k) + tok * DK,

@@ -197,17 +197,21 @@ def test_state_overlap_validates(lib):
 
 
 def test_auto_schedule(lib):
-    # chains of 25 chunks: single pass at any grid; 49: on small grids only;
-    # 64: three phases;
-    # 100: three phases; 4097 chunks: three phases
+    # chains of up to 64 chunks: single pass at any grid; 100 and 144: on
+    # large grids only (chunk-heads x N from 1.2e6); longer: three phases
     assert gla.auto_schedule(1, 6, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
     assert gla.auto_schedule(4, 6, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
     assert gla.auto_schedule(8, 12, 40, 40, 64, 64, 64) == gla.SCHED_SINGLE_PASS
     assert gla.auto_schedule(1, 6, 56, 56, 64, 64, 64) == gla.SCHED_SINGLE_PASS
-    assert gla.auto_schedule(1, 6, 64, 64, 64, 64, 64) == gla.SCHED_THREE_PHASE
-    assert gla.auto_schedule(4, 12, 56, 56, 64, 64, 64) == gla.SCHED_THREE_PHASE
+    assert gla.auto_schedule(4, 12, 56, 56, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    assert gla.auto_schedule(1, 6, 64, 64, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    assert gla.auto_schedule(8, 12, 64, 64, 64, 64, 64) == gla.SCHED_SINGLE_PASS
     assert gla.auto_schedule(1, 6, 80, 80, 64, 64, 64) == gla.SCHED_THREE_PHASE
     assert gla.auto_schedule(4, 16, 80, 80, 64, 64, 64) == gla.SCHED_THREE_PHASE
+    assert gla.auto_schedule(8, 16, 80, 80, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    assert gla.auto_schedule(1, 6, 96, 96, 64, 64, 64) == gla.SCHED_THREE_PHASE
+    assert gla.auto_schedule(4, 16, 96, 96, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    assert gla.auto_schedule(4, 16, 128, 128, 64, 64, 64) == gla.SCHED_THREE_PHASE
     assert gla.auto_schedule(1, 1, 4097, 16, 32, 32, 16) == gla.SCHED_THREE_PHASE
     # more chains than the control words hold in one launch: three phases
     assert gla.auto_schedule(1024, 64, 8, 8, 32, 32, 16) == gla.SCHED_THREE_PHASE
