@@ -39,24 +39,15 @@ def test_scan_perm_bit_exact(grid):
 
 
 # ---------------------------------------------------------------- workloads
-def _check_workload_call(w, call, bh_sample=None):
+def _check_workload_call(w, call):
     q, k, v, g = W.workload_inputs(w, call)
     dirs = w.directions(call)
-    say(f"workload {w.index} {w.name} call {call} dirs={dirs[:4]} sample={bh_sample}")
+    say(f"workload {w.index} {w.name} call {call} dirs={dirs[:4]}")
     o = run_fwd(q, k, v, g, w.grid_h, w.grid_w, dirs, w.chunk)
     assert np.all(np.isfinite(o))
-    if bh_sample is None:
-        ref = oracle.gla_forward(q, k, v, g, w.grid_h, w.grid_w, dirs)
-        got = o
-    else:
-        refs, gots = [], []
-        for b, h in bh_sample:
-            sl = lambda x: x[b:b + 1, :, h:h + 1]
-            refs.append(oracle.gla_forward(sl(q), sl(k), sl(v), sl(g), w.grid_h, w.grid_w, [dirs[b]]))
-            gots.append(o[b:b + 1, :, h:h + 1])
-        ref, got = np.concatenate(refs), np.concatenate(gots)
-    err = rel_err(got, ref)
-    say(f"  rel_err={err:.3e} cosine={cosine(got, ref):.7f}")
+    ref = oracle.gla_forward(q, k, v, g, w.grid_h, w.grid_w, dirs)
+    err = rel_err(o, ref)
+    say(f"  rel_err={err:.3e} cosine={cosine(o, ref):.7f}")
     assert err <= TOL, err
     return err
 
@@ -79,16 +70,11 @@ def test_workload3_batched_per_batch_directions():
     _check_workload_call(W.WORKLOADS[3], 0)
 
 
-def test_workload4_stack_call0_full():
-    _check_workload_call(W.WORKLOADS[4], 0)
-
-
 @pytest.mark.parametrize("call", range(12))
-def test_workload4_stack_sampled(call):
-    w = W.WORKLOADS[4]
-    rng = np.random.default_rng(500 + call)
-    sample = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)]
-    _check_workload_call(w, call, sample)
+def test_workload4_stack_full(call):
+    # every call of the 12-block stack (the directions cycle L2R, R2L, T2B,
+    # B2T), every (b, h) against the oracle
+    _check_workload_call(W.WORKLOADS[4], call)
 
 
 # ---------------------------------------------------------------- phases

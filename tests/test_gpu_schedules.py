@@ -44,6 +44,23 @@ def test_schedule_shapes_and_ragged_tail(sched, dk, dv, chunk):
     assert rel_err(o, oracle.gla_forward(*x, gh, gw, [0, 3])) <= TOL
 
 
+@pytest.mark.parametrize("B,H,g", [(8, 12, 64), (8, 16, 80), (4, 16, 96)])
+def test_auto_single_pass_on_large_grids(B, H, g):
+    # grids where gla_fwd takes the single pass with thousands of workgroups
+    # in flight (chains of 64, 100 and 144 chunks): all four directions in one
+    # launch, every (b, h) against the oracle
+    assert gla.auto_schedule(B, H, g, g, 64, 64, 64) == gla.SCHED_SINGLE_PASS
+    x = W.make_inputs(B, g * g, H, 64, 64, np.float16, seed=900 + g)
+    dirs = [b % 4 for b in range(B)]
+    say(f"auto single pass B={B} H={H} grid {g}x{g}")
+    tq, tk, tv, tg = to_dev(*x)
+    o = gla.fwd(tq, tk, tv, tg, g, g, dirs, 64)
+    torch.cuda.synchronize()
+    err = rel_err(o.double().cpu().numpy(), oracle.gla_forward(*x, g, g, dirs))
+    say(f"  rel_err={err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("wi", [0, 1, 2])
 def test_schedules_agree_on_workloads(wi):
     w = W.WORKLOADS[wi]
