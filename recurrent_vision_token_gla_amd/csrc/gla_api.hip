@@ -110,6 +110,24 @@ bool single_pass_fits(const gla::Problem& p) {
   return gla::onepass_fits(p, nb_max);
 }
 
+// Value splits of the single pass: every column of the state is its own
+// recurrence, so two workgroups per chunk-head can each take half of dv = 64
+// (the pages' operator description fixes no work split; the score tile and
+// the decay factors are recomputed by both). Worth it only while the grid
+// leaves CUs idle: measured on MI355X (64/64, chunk 64, graph-replayed over
+// rotating inputs, us per call, unsplit against split), 12.9 vs 11.1 at 54
+// chunk-heads, 13.1 vs 11.4 at 96, 12.8 vs 11.1 at 100, 13.0 vs 11.8 at 150,
+// 15.5 vs 14.5 at 216 (chains of 36 chunks), 13.4 vs 13.5 at 200, 14.6 vs
+// 14.5 at 250, 16.4 vs 17.1 at 294, 14.8 vs 15.7 at 300.
+constexpr long kSplitMaxChunks = 224;  // chunk-heads of the whole call
+
+int single_pass_splits(const gla::Problem& p, const gla::Epilogue& epi) {
+  if (p.dv != 64 || epi.gate || (long)p.B * p.H * p.N > kSplitMaxChunks) return 1;
+  gla::Problem q = p;
+  q.vs = 2;
+  return single_pass_fits(q) ? 2 : 1;
+}
+
 bool prefer_single_pass(const gla::Problem& p) {
   return p.N <= kOnepassAnyGrid ||
          (p.N <= kOnepassMaxChain && (long)p.B * p.H * p.N * p.N >= kOnepassLongWork);
@@ -208,6 +226,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* gk, void* 
   if (mode == 2) onepass = false;
   if (onepass) {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    p.vs = single_pass_splits(p, epi);
     for (int b0 = 0; b0 < B; b0 += gla::kMaxBatchPerLaunch) {
       const int nb = B - b0 < gla::kMaxBatchPerLaunch ? B - b0 : gla::kMaxBatchPerLaunch;
       const hipError_t e = gla::launch_onepass(p, b0, nb, pack_dirs(dir, b0, nb), q, k, v, gk, o,

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     float* __restrict__ Aws, half_t* __restrict__ Sws, const float* __restrict__ SigS,
     float* __restrict__ GAws, unsigned* __restrict__ ctrl, const float* s0, float* sfin,
     const InT* __restrict__ zp, const float* __restrict__ nw, float eps, int T, int H, int N,
-    int G, int nseg, int gh, int gw, DirPack dirs) {
+    int G, int nseg, int gh, int gw, DirPack dirs, int VS) {
   constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
   constexpr int NPAIR = NB * (NB - 1) / 2;
   constexpr int DKDV = DK * DV;
@@ -174,15 +174,21 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     const int ch = blockIdx.x - run * nch;
     n = run * GR + grp, h = ch % H, b = ch / H;
   } else if constexpr (kFused) {
-    // chunk-major: chunk n of every chain, then chunk n + 1
+    // chunk-major: chunk n of every chain, then chunk n + 1; with the value
+    // columns split (VS > 1), each head is VS chains of DV columns
     const int nbh = (int)(gridDim.x / N);
     n = blockIdx.x / nbh;
     const int bh = blockIdx.x - n * nbh;
-    h = bh % H, b = bh / H;
+    h = bh % (H * VS), b = bh / (H * VS);
   } else {
     n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   }
-  const long bh = (long)b * H + h, bhn = bh * N + n;
+  // this workgroup's chain (b, h) of B x (H VS) chains, its head hr and its
+  // value columns vs DV .. vs DV + DV - 1 of that head's VS DV
+  const long bh = (long)b * H * VS + h, bhn = bh * N + n;
+  const int hr = h / VS, vs = h - hr * VS, VP = DV * VS;
+  // element (d, e) of this chain's state in a [B][H][DK][VS DV] state array
+  auto st_at = [&](int d, int e) { return (((long)b * H + hr) * DK + d) * VP + vs * DV + e; };
   const int tid = GR > 1 ? (int)threadIdx.x % kThreads : (int)threadIdx.x;  // within the chunk
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4, lk = 8 * lq;
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   bool pad;  // this lane's token row is padding
   {
     const int rr = owner ? token_row(n * C + t, T, gh, gw, dir) : -1;
-    const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
+    const long row = rr >= 0 ? ((long)b * T + rr) * H + hr : -1;
     pad = row < 0;
     qr.load(qp, row, DK, lk);
     kr.load(kp, row, DK, lk);
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     for (int it = 0; it < NSIT; ++it) h8[it] = load8h(Sb + 8 * ((tid + kThreads * it) % (DKDV / 8)));
     sig_d = SigS[bhn * DK + (tid % DK)];
   }
-  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV, tid);
+  load_v<DV, C, VSTR>(vp + vs * DV, n * C, T, gh, gw, dir, (long)b * T, H, hr, VP, sV, tid);
   if constexpr (!kFused) {
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) {
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
       // in registers through the common tiers would cost more than this
       // rare reload)
       const int rr = token_row(n * C + t, T, gh, gw, dir);
-      const long row = rr >= 0 ? ((long)b * T + rr) * H + h : -1;
+      const long row = rr >= 0 ? ((long)b * T + rr) * H + hr : -1;
       float part[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) part[j] = 0.f;
@@ -735,7 +741,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
       if (x8 < DKDV) {
         if (s0) {
           float z[8];
-          load_f8(s0 + bh * DKDV + x8, z);
+          load_f8(s0 + st_at(x8 / DV, x8 % DV), z);
 #pragma unroll
           for (int c = 0; c < 8; ++c) pv[g][c] += w2[g] * z[c];
         }
@@ -745,7 +751,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
           float f[8];
 #pragma unroll
           for (int c = 0; c < 8; ++c) f[c] = sAn[d] * xs[g][c] + sSigU[d] * (float)ul[g][c];
-          store_f8(sfin + bh * DKDV + x8, f);
+          store_f8(sfin + st_at(x8 / DV, x8 % DV), f);
         }
       }
     }
@@ -811,7 +817,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
           for (int c = 0; c < 8; ++c) pv[g][c] += w * (float)u[c];
         } else if (s0) {
           float z[8];
-          load_f8(s0 + bh * DKDV + x8, z);
+          load_f8(s0 + st_at(x8 / DV, x8 % DV), z);
 #pragma unroll
           for (int c = 0; c < 8; ++c) pv[g][c] += w2[g] * z[c];
         }
@@ -836,7 +842,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
             m = fmaxf(m, fabsf(inc[c]));
           }
           if (last_run) {
-            if (sfin) store_f8(sfin + bh * DKDV + x8, inc);
+            if (sfin) store_f8(sfin + st_at(x8 / DV, x8 % DV), inc);
           } else {
             const float sg = row_scale(DV == 64 ? group_max<8>(m) : group_max<4>(m));
             const float inv = inv_scale(sg);
@@ -918,9 +924,9 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   constexpr int LPR = DV / 8;  // lanes per output row
   for (int u = tid; u < C * LPR; u += kThreads) {
     const int r = u / LPR, c8 = (u % LPR) * 8;
-    const long orow = ((long)b * T + (sRow[r] >= 0 ? sRow[r] : 0)) * H + h;
+    const long orow = (((long)b * T + (sRow[r] >= 0 ? sRow[r] : 0)) * H + hr) * VP + vs * DV;
     if constexpr (!kGate) {
-      if (sRow[r] >= 0) copy8(op + orow * DV + c8, &sO[r][c8]);
+      if (sRow[r] >= 0) copy8(op + orow + c8, &sO[r][c8]);
       continue;
     }
     float x[8];
@@ -928,7 +934,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     for (int c = 0; c < 8; ++c) x[c] = (float)sO[r][c8 + c];
     if constexpr (kGate) {
       float z[8], wn[8];
-      load8(zp + orow * DV + c8, z);
+      load8(zp + orow + c8, z);
       load_f8(nw + c8, wn);
       float ss = 0.f;
 #pragma unroll
@@ -942,7 +948,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
         x[c] *= inv * wn[c] * z[c] * sg;
       }
     }
-    if (sRow[r] >= 0) store8(op + orow * DV + c8, x);
+    if (sRow[r] >= 0) store8(op + orow + c8, x);
   }
   if constexpr (kFused && GR == 1) {
     // -- this chunk is done reading what its chain published: count it; the
@@ -981,7 +987,39 @@ hipError_t outputs_t(const Problem& p, int b0, int nb, const DirPack& dirs, cons
                      reinterpret_cast<const float*>(ws + w.off_ss) + bhn * DK,
                      nullptr, nullptr, nullptr, nullptr,
                      kGate ? static_cast<const InT*>(epi.gate) + tok * DV : nullptr,
-                     epi.weight, epi.eps, p.T, p.H, p.N, 1, 1, p.gh, p.gw, dirs);
+                     epi.weight, epi.eps, p.T, p.H, p.N, 1, 1, p.gh, p.gw, dirs, 1);
+  return hipGetLastError();
+}
+
+// One single-pass launch of chunk_kernel with DVW value columns per
+// workgroup and VS = DV / DVW workgroups per chunk-head (the workspace
+// arrays are indexed by the B x H VS chains; U tiles and states keep their
+// size, the (decay, scale) pairs are VS times as many)
+template <int DK, int DV, int DVW, int C, typename InT, bool kGate>
+hipError_t onepass_launch(const Problem& p, int b0, int nb, const DirPack& dirs, const void* q,
+                          const void* k, const void* v, const void* gk, void* o, char* ws,
+                          const float* s0, float* sfin, const Epilogue& epi, hipStream_t s) {
+  constexpr int VS = DV / DVW;
+  const WsLayout w = workspace_layout(p);
+  const Segments sg = onepass_segments(p.N);
+  const long tok = (long)b0 * p.T * p.H;
+  const long bhn = (long)b0 * p.H * VS * p.N;
+  const long bhs = (long)b0 * p.H * VS * sg.nseg;
+  const long st = (long)b0 * p.H * DK * DV;
+  // chunk-major: chunk n of every (batch, head) chain before chunk n + 1
+  dim3 grid((unsigned)((long)nb * p.H * VS * p.N));
+  hipLaunchKernelGGL((chunk_kernel<DK, DVW, C, InT, true, kGate>), grid, dim3(kThreads), 0, s,
+                     static_cast<const InT*>(q) + tok * DK, static_cast<const InT*>(k) + tok * DK,
+                     static_cast<const InT*>(v) + tok * DV, static_cast<const InT*>(gk) + tok * DK,
+                     static_cast<InT*>(o) + tok * DV,
+                     reinterpret_cast<half_t*>(ws + w.off_U) + bhn * DK * DVW,
+                     reinterpret_cast<float*>(ws + w.off_a) + 2 * bhn * DK,
+                     reinterpret_cast<half_t*>(ws + w.off_S) + bhs * DK * DVW, nullptr,
+                     reinterpret_cast<float*>(ws + w.off_g) + 2 * bhs * DK,
+                     reinterpret_cast<unsigned*>(ws), s0 ? s0 + st : nullptr,
+                     sfin ? sfin + st : nullptr,
+                     kGate ? static_cast<const InT*>(epi.gate) + tok * DV : nullptr, epi.weight,
+                     epi.eps, p.T, p.H, p.N, sg.G, sg.nseg, p.gh, p.gw, dirs, VS);
   return hipGetLastError();
 }
 
@@ -989,27 +1027,14 @@ template <int DK, int DV, int C, typename InT, bool kGate>
 hipError_t onepass_t(const Problem& p, int b0, int nb, const DirPack& dirs, const void* q,
                      const void* k, const void* v, const void* gk, void* o, char* ws,
                      const float* s0, float* sfin, const Epilogue& epi, hipStream_t s) {
-  const WsLayout w = workspace_layout(p);
-  const Segments sg = onepass_segments(p.N);
-  const long tok = (long)b0 * p.T * p.H;
-  const long bhn = (long)b0 * p.H * p.N;
-  const long bhs = (long)b0 * p.H * sg.nseg;
-  const long st = (long)b0 * p.H * DK * DV;
-  // chunk-major: chunk n of every (batch, head) chain before chunk n + 1
-  dim3 grid((unsigned)((long)nb * p.H * p.N));
-  hipLaunchKernelGGL((chunk_kernel<DK, DV, C, InT, true, kGate>), grid, dim3(kThreads), 0, s,
-                     static_cast<const InT*>(q) + tok * DK, static_cast<const InT*>(k) + tok * DK,
-                     static_cast<const InT*>(v) + tok * DV, static_cast<const InT*>(gk) + tok * DK,
-                     static_cast<InT*>(o) + tok * DV,
-                     reinterpret_cast<half_t*>(ws + w.off_U) + bhn * DK * DV,
-                     reinterpret_cast<float*>(ws + w.off_a) + 2 * bhn * DK,
-                     reinterpret_cast<half_t*>(ws + w.off_S) + bhs * DK * DV, nullptr,
-                     reinterpret_cast<float*>(ws + w.off_g) + 2 * bhs * DK,
-                     reinterpret_cast<unsigned*>(ws), s0 ? s0 + st : nullptr,
-                     sfin ? sfin + st : nullptr,
-                     kGate ? static_cast<const InT*>(epi.gate) + tok * DV : nullptr, epi.weight,
-                     epi.eps, p.T, p.H, p.N, sg.G, sg.nseg, p.gh, p.gw, dirs);
-  return hipGetLastError();
+  if constexpr (DV == 64 && !kGate) {
+    if (p.vs == 2)
+      return onepass_launch<DK, DV, DV / 2, C, InT, kGate>(p, b0, nb, dirs, q, k, v, gk, o, ws,
+                                                           s0, sfin, epi, s);
+  }
+  if (p.vs != 1) return hipErrorInvalidValue;
+  return onepass_launch<DK, DV, DV, C, InT, kGate>(p, b0, nb, dirs, q, k, v, gk, o, ws, s0, sfin,
+                                                   epi, s);
 }
 
 #define GLA_DISPATCH(FN, ...)                                                          \

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     kr.load(kp, row, DK, lk);
     gr.load(gp, row, DK, lk);
   }
-  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, sV, threadIdx.x);
+  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, DV, sV, threadIdx.x);
   if (tid < DK) sRowMax[tid] = 0u;
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
     kr.zero_if(pad);
@@ -450,7 +450,7 @@ WsLayout workspace_layout(const Problem& p) {
   WsLayout w;
   w.off_U = (size_t)kCtrlWords * sizeof(unsigned);
   w.off_a = w.off_U + up(units * p.dk * p.dv * sizeof(half_t));
-  w.off_S = w.off_a + up(units * p.dk * 2 * sizeof(float));
+  w.off_S = w.off_a + up(units * p.dk * 2 * sizeof(float) * (p.dv == 64 ? 2 : 1));
   w.off_g = w.off_S + up(units * p.dk * p.dv * sizeof(half_t));
   w.off_ss = w.off_g + up(units * p.dk * 2 * sizeof(float));
   w.total = w.off_ss + up(units * p.dk * sizeof(float));
@@ -469,8 +469,9 @@ Segments onepass_segments(int N) {
 bool onepass_fits(const Problem& p, int nb) {
   const Segments sg = onepass_segments(p.N);
   if (sg.G > 64 || sg.nseg > 64) return false;  // one wave watches every flag it waits on
-  const long words = kCtrlHeader + (long)nb * p.H * (p.N + sg.nseg + 1);
-  return words <= kCtrlWords && (long)nb * p.H * p.N <= 0x7fffffffL;
+  const long chains = (long)nb * p.H * p.vs;
+  const long words = kCtrlHeader + chains * (p.N + sg.nseg + 1);
+  return words <= kCtrlWords && chains * p.N <= 0x7fffffffL;
 }
 
 hipError_t launch_summaries(const Problem& p, int b0, int nb, const DirPack& dirs,

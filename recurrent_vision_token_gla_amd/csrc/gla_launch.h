@@ -12,13 +12,15 @@ namespace gla {
 
 struct Problem {
   int B, H, gh, gw, T, dk, dv, chunk, N;
-  int dtype;  // GLA_F16 or GLA_F32
+  int dtype;   // GLA_F16 or GLA_F32
+  int vs = 1;  // single pass: workgroups per chunk-head, each on dv / vs value columns
 };
 
 // Byte offsets of the arrays inside the workspace: the control words (fixed
 // size, offset 0), U (half rows divided by their scales), the pairs
-// (a_n[d], row scale of U_n row d) as float2 [B][H][N][dk], S (S also holds
-// the single-pass segment aggregates), the single-pass segment pairs
+// (a_n[d], row scale of U_n row d) as float2 [B][H][N][dk] (twice that for
+// dv = 64, whose single pass may split the value columns in two), S (S also
+// holds the single-pass segment aggregates), the single-pass segment pairs
 // (decay, row scale), and the row scales of the three-phase S (float
 // [B][H][N][dk]). Every scale is a power of two.
 struct WsLayout {
@@ -34,7 +36,7 @@ struct Segments {
 };
 Segments onepass_segments(int N);
 // Whether a launch of nb batch elements fits the single-pass schedule's
-// control words and wait width.
+// control words and wait width (with p.vs chains per (batch, head)).
 bool onepass_fits(const Problem& p, int nb);
 
 // Each launcher enqueues one phase for batch elements [b0, b0 + nb) of the

@@ -126,9 +126,11 @@ __device__ __forceinline__ half4 ld_tr(const half_t* blk) {
 // (half, zero for padding rows) with 16-byte stores; each thread finds its
 // rows' raster positions itself, and the loads are unconditional as in
 // load_row (tix: the thread's index among the chunk's kThreads threads).
+// A (token, head) row of v holds `pitch` elements, DV of them read here.
 template <int DV, int C, int VSTR, typename InT>
 __device__ __forceinline__ void load_v(const InT* vp, int tok0, int T, int gh, int gw, int dir,
-                                       long bT, int H, int h, half_t (*sV)[VSTR], int tix) {
+                                       long bT, int H, int h, int pitch, half_t (*sV)[VSTR],
+                                       int tix) {
   constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
   half8 v8[NIT];
   int rows[NIT];
@@ -137,7 +139,7 @@ __device__ __forceinline__ void load_v(const InT* vp, int tok0, int T, int gh, i
     const int u = tix + kThreads * it;
     const int r = (u / (DV / 8)) % C, c8 = (u % (DV / 8)) * 8;
     rows[it] = token_row(tok0 + r, T, gh, gw, dir);
-    v8[it] = load8h(vp + ((bT + (rows[it] >= 0 ? rows[it] : 0)) * H + h) * DV + c8);
+    v8[it] = load8h(vp + ((bT + (rows[it] >= 0 ? rows[it] : 0)) * H + h) * pitch + c8);
   }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {

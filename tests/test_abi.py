@@ -47,15 +47,20 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # control words (64 KiB) + U (f16) + (a, U row scale) pairs (2 x f32) + S (f16)
-    # + single-pass segment pairs (2 x f32) + S row scales (f32), each padded to
-    # 256 bytes
+    # control words (64 KiB) + U (f16) + (a, U row scale) pairs (2 x f32; twice
+    # as many for dv = 64, whose single pass may split the value columns in
+    # two) + S (f16) + single-pass segment pairs (2 x f32) + S row scales
+    # (f32), each padded to 256 bytes
     B, H, gh, gw, dk, dv, C = 1, 6, 40, 40, 64, 64, 64
     N = 25
     units = B * H * N
-    expect = (65536 + units * dk * dv * 2 + units * dk * 8 + units * dk * dv * 2
+    expect = (65536 + units * dk * dv * 2 + 2 * units * dk * 8 + units * dk * dv * 2
               + units * dk * 8 + units * dk * 4)
     assert gla.workspace_bytes(B, H, gh, gw, dk, dv, C) == expect
+    units32 = 1 * 1 * 4  # 8x8 grid, chunk 16, dv = 32: one set of pairs
+    assert gla.workspace_bytes(1, 1, 8, 8, 32, 32, 16) == (
+        65536 + units32 * 32 * 32 * 2 + units32 * 32 * 8 + units32 * 32 * 32 * 2
+        + units32 * 32 * 8 + units32 * 32 * 4)
     assert gla.workspace_bytes(0, H, gh, gw, dk, dv, C) == 0
     assert gla.workspace_bytes(1, 1, 5, 7, 32, 32, 16) > 0
     assert gla.workspace_bytes(1, 1, 8, 8, 48, 32, 16) == 0  # unsupported dk

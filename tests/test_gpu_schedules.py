@@ -44,6 +44,24 @@ def test_schedule_shapes_and_ragged_tail(sched, dk, dv, chunk):
     assert rel_err(o, oracle.gla_forward(*x, gh, gw, [0, 3])) <= TOL
 
 
+@pytest.mark.parametrize("H", [8, 10])
+@pytest.mark.parametrize("dv", [32, 64])
+def test_single_pass_value_split_both_sides(H, dv):
+    # 40x40 grid: H 8 is 200 chunk-heads (dv = 64 splits its value columns
+    # over two workgroups per chunk-head), H 10 is 250 (no split); with a
+    # carried state in and out, against the oracle
+    g, B = 40, 1
+    x = W.make_inputs(B, g * g, H, 64, dv, np.float16, seed=950 + H + dv)
+    s0 = np.random.default_rng(7).standard_normal((B, H, 64, dv)).astype(np.float32)
+    dirs = [2]
+    say(f"single pass H={H} dv={dv}")
+    o, sT = _run(x, g, g, dirs, 64, gla.SCHED_SINGLE_PASS, s0=s0)
+    ref, refT = oracle.gla_forward(*x, g, g, dirs, s0=s0, return_state=True)
+    e, eT = rel_err(o, ref), rel_err(sT, refT)
+    say(f"  rel_err={e:.3e} state {eT:.3e}")
+    assert e <= TOL and eT <= TOL
+
+
 @pytest.mark.parametrize("B,H,g", [(8, 12, 64), (8, 16, 80), (4, 16, 96)])
 def test_auto_single_pass_on_large_grids(B, H, g):
     # grids where gla_fwd takes the single pass with thousands of workgroups
