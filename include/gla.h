@@ -58,8 +58,11 @@
  * from the summaries its predecessors publish (grouped in about sqrt(N)
  * segments, whose last chunks publish segment aggregates), and adds the
  * readout. Workgroups run in chunk-major order (chunk n of every chain,
- * then chunk n + 1) and only wait on earlier ones, with bounded waits.
- * gla_fwd_schedule and gla_auto_schedule say which one a call takes.
+ * then chunk n + 1) and only wait on earlier ones, with bounded waits. On
+ * small grids with dv = 64 (at most 224 chunk-heads, no output gate) each
+ * chunk-head runs as two workgroups of 32 value columns (the columns of the
+ * state are independent recurrences). gla_fwd_schedule and
+ * gla_auto_schedule say which schedule a call takes.
  *
  * Workspace: caller-owned device memory of gla_fwd_workspace_bytes bytes,
  * 256-byte aligned, of ANY contents. Its first 64 KiB are the single pass's
