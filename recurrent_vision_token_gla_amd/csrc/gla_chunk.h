@@ -58,14 +58,14 @@ namespace tile {
 //      (the other chunks compute theirs while the aggregates arrive);
 //   3. adds the readout Q^ S_n and stores the outputs.
 // ===========================================================================
-template <int DK, int DV, int C, typename InT, bool kFused, bool kGate, int GR = 1>
+template <int DK, int DV, int C, typename InT, bool kFused, bool kGate, int GR = 1, int VS = 1>
 __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     const InT* __restrict__ qp, const InT* __restrict__ kp, const InT* __restrict__ vp,
     const InT* __restrict__ gp, InT* __restrict__ op, half_t* __restrict__ Uws,
     float* __restrict__ Aws, half_t* __restrict__ Sws, const float* __restrict__ SigS,
     float* __restrict__ GAws, unsigned* __restrict__ ctrl, const float* s0, float* sfin,
     const InT* __restrict__ zp, const float* __restrict__ nw, float eps, int T, int H, int N,
-    int G, int nseg, int gh, int gw, DirPack dirs, int VS) {
+    int G, int nseg, int gh, int gw, DirPack dirs) {
   constexpr int NB = C / 16, NKS = DK / 32, NEL = 8 * NKS, NE = DV / 16, ND = DK / 16;
   constexpr int NPAIR = NB * (NB - 1) / 2;
   constexpr int DKDV = DK * DV;
@@ -186,7 +186,8 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   // this workgroup's chain (b, h) of B x (H VS) chains, its head hr and its
   // value columns vs DV .. vs DV + DV - 1 of that head's VS DV
   const long bh = (long)b * H * VS + h, bhn = bh * N + n;
-  const int hr = h / VS, vs = h - hr * VS, VP = DV * VS;
+  const int hr = h / VS, vs = h - hr * VS;
+  constexpr int VP = DV * VS;
   // element (d, e) of this chain's state in a [B][H][DK][VS DV] state array
   auto st_at = [&](int d, int e) { return (((long)b * H + hr) * DK + d) * VP + vs * DV + e; };
   const int tid = GR > 1 ? (int)threadIdx.x % kThreads : (int)threadIdx.x;  // within the chunk
@@ -987,7 +988,7 @@ hipError_t outputs_t(const Problem& p, int b0, int nb, const DirPack& dirs, cons
                      reinterpret_cast<const float*>(ws + w.off_ss) + bhn * DK,
                      nullptr, nullptr, nullptr, nullptr,
                      kGate ? static_cast<const InT*>(epi.gate) + tok * DV : nullptr,
-                     epi.weight, epi.eps, p.T, p.H, p.N, 1, 1, p.gh, p.gw, dirs, 1);
+                     epi.weight, epi.eps, p.T, p.H, p.N, 1, 1, p.gh, p.gw, dirs);
   return hipGetLastError();
 }
 
@@ -1008,7 +1009,7 @@ hipError_t onepass_launch(const Problem& p, int b0, int nb, const DirPack& dirs,
   const long st = (long)b0 * p.H * DK * DV;
   // chunk-major: chunk n of every (batch, head) chain before chunk n + 1
   dim3 grid((unsigned)((long)nb * p.H * VS * p.N));
-  hipLaunchKernelGGL((chunk_kernel<DK, DVW, C, InT, true, kGate>), grid, dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((chunk_kernel<DK, DVW, C, InT, true, kGate, 1, VS>), grid, dim3(kThreads), 0, s,
                      static_cast<const InT*>(q) + tok * DK, static_cast<const InT*>(k) + tok * DK,
                      static_cast<const InT*>(v) + tok * DV, static_cast<const InT*>(gk) + tok * DK,
                      static_cast<InT*>(o) + tok * DV,
@@ -1019,7 +1020,7 @@ hipError_t onepass_launch(const Problem& p, int b0, int nb, const DirPack& dirs,
                      reinterpret_cast<unsigned*>(ws), s0 ? s0 + st : nullptr,
                      sfin ? sfin + st : nullptr,
                      kGate ? static_cast<const InT*>(epi.gate) + tok * DV : nullptr, epi.weight,
-                     epi.eps, p.T, p.H, p.N, sg.G, sg.nseg, p.gh, p.gw, dirs, VS);
+                     epi.eps, p.T, p.H, p.N, sg.G, sg.nseg, p.gh, p.gw, dirs);
   return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ hipError_t runs_t(const Problem& p, int b0, int nb, const DirPack& dirs, const v
                      reinterpret_cast<float*>(ws + w.off_g) + 2 * bhr * DK,
                      reinterpret_cast<unsigned*>(ws), s0 ? s0 + st : nullptr,
                      sfin ? sfin + st : nullptr, nullptr, nullptr, 0.f, p.T, p.H, p.N, GR, NS,
-                     p.gh, p.gw, dirs, 1);
+                     p.gh, p.gw, dirs);
   return hipGetLastError();
 }
 
