@@ -12,7 +12,10 @@ namespace gla {
 namespace tile {
 
 // ===========================================================================
-// Chunk outputs. One workgroup per (chunk n, head h, batch b).
+// Chunk outputs. One workgroup per (chunk n, head h, batch b), or VS of
+// them, each on DV of the head's VS DV value columns (VS > 1: the single
+// pass's value split; every column of the state is its own recurrence, so
+// the workgroups share nothing but their q, k, gk inputs).
 //   O = A V + Q^ S_n,   A = causal decayed score tile
 //
 // Wave w owns query sub-block I = w (tokens 16I..16I+15). A lane holds one
@@ -32,9 +35,10 @@ namespace tile {
 // half operands while no key dim decays by more than 2^8 over the block and
 // max(|Q~|, |K~|) * 2^range stays within 2^15, float operands while the range
 // is within 2^120 and those factors stay finite, and beyond that a direct
-// float sum of every entry from 2^(s_i - s_j) (q and k read again). Score entries beyond 2^14 in
-// magnitude make the wave divide its score blocks by a power of two sigA,
-// undone on the accumulators (the product with V is linear).
+// float sum of every entry from 2^(s_i - s_j) (q and k read again). Score
+// entries beyond 2^14 in magnitude make the wave divide its score blocks by a
+// power of two sigA, undone on the accumulators (the product with V is
+// linear).
 //
 // The three-phase entering state S_n arrives as half rows divided by their
 // power-of-two scales sigS[d] >= 1. The readout folds sigS[d] / max_d sigS
