@@ -45,6 +45,24 @@ def _device():
     yield
 
 
+def _gated_err(yg, yr, ro, z, w):
+    """The gated output's error against the bar: max|y - y_ref| / max|y_ref|
+    over the rows whose RMS is at least 1/8 of max|o_ref|; a row with a
+    smaller RMS (o nearly cancels there) is held to o's bar carried through
+    the normalisation, 2 TOL max|o_ref| max|w silu(z)| / rms_row, and reports
+    its error scaled to that bound (TOL when at the bound)."""
+    rms = np.sqrt(np.mean(ro * ro, axis=-1, keepdims=True))
+    big = np.abs(ro).max()
+    ok = rms[..., 0] >= big / 8
+    d = np.abs(yg - yr)
+    err = d[ok].max() / np.abs(yr).max() if ok.any() else 0.0
+    if not ok.all():
+        g = np.abs(w.astype(np.float64) * z / (1 + np.exp(-z.astype(np.float64)))).max(-1, keepdims=True)
+        bound = 2 * TOL * big * g / np.maximum(rms, 1e-300)
+        err = max(err, TOL * (d / bound)[~ok].max())
+    return err
+
+
 @pytest.mark.parametrize("i", range(NCASES))
 def test_random_case(i):
     c = _case(i)
@@ -65,7 +83,8 @@ def test_random_case(i):
         y = gla.fwd_gated(tq, tk, tv, tg, tz, tw, W.GATE_EPS, c["gh"], c["gw"], c["dirs"],
                           chunk=c["chunk"], s0=ts0, s_final=sT)
         torch.cuda.synchronize()
-        err = rel_err(y.double().cpu().numpy(), oracle.rmsnorm_gate(ro, z, w, W.GATE_EPS))
+        yg, yr = y.double().cpu().numpy(), oracle.rmsnorm_gate(ro, z, w, W.GATE_EPS)
+        err = _gated_err(yg, yr, ro, z, w)
     else:
         o, sT = gla.fwd_state(tq, tk, tv, tg, c["gh"], c["gw"], c["dirs"], chunk=c["chunk"], s0=ts0,
                               schedule=c["sched"])
