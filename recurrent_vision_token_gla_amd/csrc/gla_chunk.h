@@ -220,30 +220,27 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     kr.load(kp, row, DK, lk);
     gr.load(gp, row, DK, lk);
   }
-  // -- the entering state (stored [dk][dv], staged as rows sS[d][e]; three-
-  // phase schedule only) and the chunk's V rows, through LDS; every load is
-  // issued before the first LDS write that waits on one
+  // -- the row scales and the entering state (stored [dk][dv], staged as
+  // rows sS[d][e]; three-phase schedule only) and the chunk's V rows, all
+  // loaded now; the state and (see kDeferV) the V rows are written to LDS
+  // after the decay scan, which so waits only for the q, k, gk rows issued
+  // before them
   constexpr int NSIT = kFused ? 1 : (DKDV / 8 + kThreads - 1) / kThreads;
   half8 h8[NSIT];
   float sig_d = 1.f;  // thread d < DK: row scale of S_n row d
   if constexpr (!kFused) {
+    sig_d = SigS[bhn * DK + (tid % DK)];
     const half_t* Sb = Sws + bhn * (long)DKDV;
 #pragma unroll
     for (int it = 0; it < NSIT; ++it) h8[it] = load8h(Sb + 8 * ((tid + kThreads * it) % (DKDV / 8)));
-    sig_d = SigS[bhn * DK + (tid % DK)];
   }
-  load_v<DV, C, VSTR>(vp + vs * DV, n * C, T, gh, gw, dir, (long)b * T, H, hr, VP, sV, tid);
-  if constexpr (!kFused) {
-#pragma unroll
-    for (int it = 0; it < NSIT; ++it) {
-      const int u = tid + kThreads * it;
-      if (u < DKDV / 8) {
-        const int d = u / (DV / 8), e8 = (u % (DV / 8)) * 8;
-        *reinterpret_cast<half8*>(&sS[d][e8]) = h8[it];
-      }
-    }
-    if (tid < DK) sSig[tid] = sig_d;
-  }
+  VRows<DV, C, VSTR, InT> vrows;
+  vrows.load(vp + vs * DV, n * C, T, gh, gw, dir, (long)b * T, H, hr, VP, tid);
+  // (three-phase kernels with half inputs; with float inputs and in the
+  // runs kernel there are no registers to spare, and the single pass gains
+  // nothing measurable from it: their V rows go to LDS at once)
+  constexpr bool kDeferV = sizeof(InT) == 2 && GR == 1 && !kFused;
+  if constexpr (!kDeferV) vrows.store(n * C, T, sV, tid);
 
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
     qr.zero_if(pad);
@@ -263,6 +260,18 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
       }
     }
   }
+  if constexpr (!kFused) {
+#pragma unroll
+    for (int it = 0; it < NSIT; ++it) {
+      const int u = tid + kThreads * it;
+      if (u < DKDV / 8) {
+        const int d = u / (DV / 8), e8 = (u % (DV / 8)) * 8;
+        *reinterpret_cast<half8*>(&sS[d][e8]) = h8[it];
+      }
+    }
+    if (tid < DK) sSig[tid] = sig_d;
+  }
+  if constexpr (kDeferV) vrows.store(n * C, T, sV, tid);
   __syncthreads();
 
   // -- per (sub-block, key dim) factors, one key dim per thread

@@ -87,7 +87,11 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
     kr.load(kp, row, DK, lk);
     gr.load(gp, row, DK, lk);
   }
-  load_v<DV, C, VSTR>(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, DV, sV, threadIdx.x);
+  // V rows: written to LDS after the decay scan (float inputs: at once,
+  // they have no registers to spare)
+  VRows<DV, C, VSTR, InT> vrows;
+  vrows.load(vp, n * C, T, gh, gw, dir, (long)b * T, H, h, DV, threadIdx.x);
+  if constexpr (sizeof(InT) == 4) vrows.store(n * C, T, sV, threadIdx.x);
   if (tid < DK) sRowMax[tid] = 0u;
   if ((n + 1) * C > T) {  // the chain's last chunk: zero the padding rows
     kr.zero_if(pad);
@@ -101,6 +105,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
       for (int e = 0; e < NEL; ++e) sTot[I][32 * (e / 8) + lk + (e % 8)] = sc[e];
     }
   }
+  if constexpr (sizeof(InT) == 2) vrows.store(n * C, T, sV, threadIdx.x);
   __syncthreads();
 
   const long bhn = ((long)b * H + h) * N + n;

@@ -122,36 +122,42 @@ __device__ __forceinline__ half4 ld_tr(const half_t* blk) {
   return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)p));
 }
 
-// V rows of the chunk (scan positions tok0..tok0+C-1) into sV[token][e]
-// (half, zero for padding rows) with 16-byte stores; each thread finds its
-// rows' raster positions itself, and the loads are unconditional as in
-// load_row (tix: the thread's index among the chunk's kThreads threads).
-// A (token, head) row of v holds `pitch` elements, DV of them read here.
+// V rows of the chunk (scan positions tok0..tok0+C-1) for sV[token][e]
+// (half, zero for padding rows), in two steps: load() issues the 16-byte
+// loads into registers (each thread finds its rows' raster positions itself,
+// and the loads are unconditional as in RawRow), store() writes them to LDS.
+// Work that needs only earlier loads (the decay scan) goes between the two,
+// so it does not wait for V. tix: the thread's index among the chunk's
+// kThreads threads; a (token, head) row of v holds `pitch` elements, DV of
+// them read here.
 template <int DV, int C, int VSTR, typename InT>
-__device__ __forceinline__ void load_v(const InT* vp, int tok0, int T, int gh, int gw, int dir,
-                                       long bT, int H, int h, int pitch, half_t (*sV)[VSTR],
-                                       int tix) {
-  constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
+struct VRows {
+  static constexpr int NIT = (C * (DV / 8) + kThreads - 1) / kThreads;
   half8 v8[NIT];
   int rows[NIT];
+  __device__ __forceinline__ void load(const InT* vp, int tok0, int T, int gh, int gw, int dir,
+                                       long bT, int H, int h, int pitch, int tix) {
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int u = tix + kThreads * it;
-    const int r = (u / (DV / 8)) % C, c8 = (u % (DV / 8)) * 8;
-    rows[it] = token_row(tok0 + r, T, gh, gw, dir);
-    v8[it] = load8h(vp + ((bT + (rows[it] >= 0 ? rows[it] : 0)) * H + h) * pitch + c8);
-  }
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int u = tix + kThreads * it;
-    const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
-    if (u < C * (DV / 8)) {
-      half8 x = v8[it];
-      if (tok0 + C > T && rows[it] < 0) x = half8{};  // padding row (last chunk only)
-      *reinterpret_cast<half8*>(&sV[r][c8]) = x;
+    for (int it = 0; it < NIT; ++it) {
+      const int u = tix + kThreads * it;
+      const int r = (u / (DV / 8)) % C, c8 = (u % (DV / 8)) * 8;
+      rows[it] = token_row(tok0 + r, T, gh, gw, dir);
+      v8[it] = load8h(vp + ((bT + (rows[it] >= 0 ? rows[it] : 0)) * H + h) * pitch + c8);
     }
   }
-}
+  __device__ __forceinline__ void store(int tok0, int T, half_t (*sV)[VSTR], int tix) const {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int u = tix + kThreads * it;
+      const int r = u / (DV / 8), c8 = (u % (DV / 8)) * 8;
+      if (u < C * (DV / 8)) {
+        half8 x = v8[it];
+        if (tok0 + C > T && rows[it] < 0) x = half8{};  // padding row (last chunk only)
+        *reinterpret_cast<half8*>(&sV[r][c8]) = x;
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ void load_f8(const float* p, float (&a)[8]) {
   const float4 x = *reinterpret_cast<const float4*>(p);
