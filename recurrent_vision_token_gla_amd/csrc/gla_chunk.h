@@ -250,8 +250,8 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   // -- in-sub-block inclusive cumsum along tokens (DPP row scan), in log2
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(gr[e] * kLog2e);
-    if (lr == 15 || lr == 7) {
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(mulw(gr[e], kLog2e));
+    if ((lr | 8) == 15) {  // lr 15 or 7: one compare, no branch between the scan's steps
 #pragma unroll
       for (int e = 0; e < NEL; ++e) {
         const int d = 32 * (e / 8) + lk + (e % 8);
@@ -316,22 +316,25 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
   // -- per-element factors; K~ goes to LDS for the other sub-blocks, and in
   // one pass K^ = K~ 2^(totals of the later sub-blocks), for U
   float qt[NEL], kt[NEL];
-  // this lane's decay range over its sub-block (log2) and max(|Q~|, |K~|)
+  // this lane's decay range over its sub-block (log2) and max(|Q~|, |K~|);
+  // the totals are <= 0, so the largest magnitude is the largest bit pattern
   float rng = 0.f, bigt = 0.f;
   if (owner) {
+    unsigned rbits = 0u;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       float tt[8], ff[8];
       lds8(&sTot[I][32 * ks + lk], tt);
 #pragma unroll
-      for (int c = 0; c < 8; c += 2) rng = max3f(rng, -tt[c], -tt[c + 1]);
+      for (int c = 0; c < 8; c += 2)
+        rbits = max(rbits, max(__float_as_uint(tt[c]), __float_as_uint(tt[c + 1])));
       if constexpr (kFused) lds8(&sF[I][32 * ks + lk], ff);
       half8 k8, kh8;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int e = 8 * ks + c;
-        qt[e] = qr[e] * fexp2(sc[e]);
-        kt[e] = kr[e] * fexp2(tt[c] - sc[e]);
+        qt[e] = mulw(qr[e], fexp2(sc[e]));
+        kt[e] = mulw(kr[e], fexp2(tt[c] - sc[e]));
         bigt = max3f(bigt, fabsf(qt[e]), fabsf(kt[e]));
         k8[c] = (half_t)kt[e];
         if constexpr (kFused) kh8[c] = (half_t)(kt[e] * ff[c]);
@@ -339,6 +342,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
       *reinterpret_cast<half8*>(&sKt[t][32 * ks + lk]) = k8;
       if constexpr (kFused) *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = kh8;
     }
+    rng = __uint_as_float(rbits & 0x7fffffffu);
   }
   __syncthreads();
 

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
   }
   if (owner) {
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(gr[e] * kLog2e);
+    for (int e = 0; e < NEL; ++e) sc[e] = row_scan16(mulw(gr[e], kLog2e));
     if (lr == 15) {
 #pragma unroll
       for (int e = 0; e < NEL; ++e) sTot[I][32 * (e / 8) + lk + (e % 8)] = sc[e];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
       half8 kh8;
 #pragma unroll
       for (int c = 0; c < 8; ++c)  // B - b_t: the decay of the later tokens
-        kh8[c] = (half_t)(kr[8 * ks + c] * fexp2(aft[c] - sc[8 * ks + c]));
+        kh8[c] = (half_t)mulw(kr[8 * ks + c], fexp2(aft[c] - sc[8 * ks + c]));
       *reinterpret_cast<half8*>(&sKh[t][32 * ks + lk]) = kh8;
     }
   }

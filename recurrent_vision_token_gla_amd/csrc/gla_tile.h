@@ -13,13 +13,20 @@ namespace tile {
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float row_scan16(float x) {
-  // inclusive prefix sum over the 16 lanes of each DPP row
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+  // inclusive prefix sum over the 16 lanes of each DPP row; a lane whose
+  // source lies before the row's start reads 0 (bound_ctrl), which lets each
+  // step compile to one add with the shifted operand
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
   return x;
 }
+
+// x * y as a fused multiply-add with +0: the same value up to the sign of a
+// zero result, and, with x converted from a half input, one mixed-precision
+// fma instead of a conversion and a product
+__device__ __forceinline__ float mulw(float x, float y) { return fmaf(x, y, 0.f); }
 
 // Eight consecutive floats of an LDS row (16-byte aligned) in two reads.
 // Per-(sub-block, key dim) factors are fetched this way: eight scalar reads
