@@ -944,7 +944,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
     const int r = u / LPR, c8 = (u % LPR) * 8;
     const long orow = (((long)b * T + (sRow[r] >= 0 ? sRow[r] : 0)) * H + hr) * VP + vs * DV;
     if constexpr (!kGate) {
-      if (sRow[r] >= 0) copy8(op + orow + c8, &sO[r][c8]);
+      if (sRow[r] >= 0) out8(op + orow + c8, &sO[r][c8]);
       continue;
     }
     float x[8];
@@ -966,7 +966,7 @@ __global__ __launch_bounds__(kThreads * GR, 4 / GR) void chunk_kernel(
         x[c] *= inv * wn[c] * z[c] * sg;
       }
     }
-    if (sRow[r] >= 0) store8(op + orow + c8, x);
+    if (sRow[r] >= 0) out8(op + orow + c8, x);
   }
   if constexpr (kFused && GR == 1) {
     // -- this chunk is done reading what its chain published: count it; the

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void ssw_kernel(const InT* __restrict__ a
       float out[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) out[c] = silu(av[c]) * acc[c];
-      store8(hp + (bT + (long)y * gw + x) * F + cg, out);
+      out8(hp + (bT + (long)y * gw + x) * F + cg, out);
     }
   }
 }
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 3) void ssw_persistent(
         float out[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) out[c] = silu((float)av[i][c]) * acc[c];
-        store8(hp + (bT + (long)y * gw + x) * F + cg, out);
+        out8(hp + (bT + (long)y * gw + x) * F + cg, out);
       }
       if (more) av[i] = load_a(nxt, i);
     }
