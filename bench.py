@@ -211,10 +211,13 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
         lat.append(a.elapsed_time(b) * 1e3)
 
     # per-kernel durations: each kernel alone, `timing_reps` launches captured
-    # back to back in one graph (no host gaps) on the rotating sets, timed
-    # with events on the stream the kernels are launched on; and the same on
-    # the first set alone. The step's own schedule is the one gla_fwd picks;
-    # the other schedules' kernels are timed for reference.
+    # back to back in one graph (no host gaps), cycling through every call of
+    # every rotating set (the step's directions and inputs, so the inputs
+    # come from HBM as in the step), timed with events on the stream the
+    # kernels are launched on; and the step's first call repeated on one set
+    # (cache-warm). The step's own schedule is the one gla_fwd picks; the
+    # other schedules' kernels are timed for reference.
+    flat = [cs[i] for cs in sets for i in range(len(cs))]
     sched = gla.auto_schedule(w.B, w.H, w.grid_h, w.grid_w, w.dk, w.dv, w.chunk)
 
     def phase(name, c0, s):
@@ -234,7 +237,7 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
     def time_phase(name, rot):
         def fn(s):
             for r in range(timing_reps):
-                phase(name, sets[r % nsets][0] if rot else calls[0], s)
+                phase(name, flat[r % len(flat)] if rot else calls[0], s)
         pg = _graph(torch, stream, fn)
         pg.replay()
         torch.cuda.synchronize()
