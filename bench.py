@@ -16,7 +16,10 @@ stream, mirroring the pages' protocol of event timing under graph replay
 (GTR project page, "Accuracy-Latency Frontier"). The headline rotates
 through copies of the step's inputs and outputs that together exceed twice
 the 256 MB Infinity Cache, so the bytes come from HBM; the same steps on one
-set of buffers (cache-warm) are reported beside it. One JSON line is printed.
+set of buffers (cache-warm) are reported beside it. By default the headline
+times 20,000 steps (about a second of replays) and each other workload as
+many steps as fill about a second, from a short timed pilot. One JSON line
+is printed.
 
   python bench.py [--steps K] [--warmup W] [--workload I] [--no-also]
 """
@@ -162,7 +165,7 @@ def _time_steps(torch, runs, steps, warmup):
     return t0.elapsed_time(t1) / steps, time.perf_counter() - wall0
 
 
-def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
+def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30, max_seconds=None):
     dev = torch.device("cuda:0")
     calls = []
     for c in range(w.calls):
@@ -195,6 +198,12 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
     else:
         runs = [lambda cs=cs: step(cs) for cs in sets]
 
+    # with max_seconds: as many steps (at most `steps`, at least 10) as fill
+    # about that long, from a short timed pilot
+    if max_seconds:
+        pilot_ms, _ = _time_steps(torch, runs, 5, 2)
+        steps = max(10, min(steps, int(max_seconds * 1e3 / max(pilot_ms, 1e-3))))
+        warmup = min(warmup, steps)
     # headline: the sets in rotation; then the first set alone (cache-warm)
     ms_per_step, wall = _time_steps(torch, runs, steps, warmup)
     warm_ms, _ = _time_steps(torch, runs[:1], steps, warmup)
@@ -263,7 +272,8 @@ def run_workload(w, steps, warmup, use_graph, torch, gla, W, timing_reps=30):
     step(calls)
     torch.cuda.synchronize()
     used = ["single_pass"] if sched == gla.SCHED_SINGLE_PASS else ["summaries", "scan", "outputs"]
-    return dict(calls=calls, ms_per_step=ms_per_step, warm_ms_per_step=warm_ms, wall_s=wall,
+    return dict(calls=calls, steps=steps, ms_per_step=ms_per_step, warm_ms_per_step=warm_ms,
+                wall_s=wall,
                 lat_us=lat, phase_us=phase_us, phase_warm_us=phase_warm_us, ws=ws, used=used,
                 sets=nsets, set_bytes=step_bytes,
                 schedule="single_pass" if sched == gla.SCHED_SINGLE_PASS else "three_phase")
@@ -452,8 +462,8 @@ def summarize(w, res):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=1, help="index into workloads.WORKLOADS")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -519,14 +529,14 @@ def main():
     for i in extra:
         wi = W.WORKLOADS[i]
         ri = run_workload(wi, max(10, args.steps // 4), max(3, args.warmup // 4),
-                          not args.no_graph, torch, gla, W)
+                          not args.no_graph, torch, gla, W, max_seconds=1.0)
         si = summarize(wi, ri)
         print(f"# {wi.name}: {si['value']:.4g} tokens/s, {si['call_us']:.2f} us/call "
               f"({si['rotation']['sets']} rotating sets; warm {si['warm']['call_us']:.2f}), path "
               f"{100 * si['path_roofline']['frac']:.1f}% of HBM roofline, {si['schedule']}; kernels "
               + ", ".join(f"{k} {v:.2f} us" for k, v in si["phase_us"].items()),
               file=sys.stderr, flush=True)
-        also.append({"workload": wi.name, "tokens_per_call": wi.B * wi.T,
+        also.append({"workload": wi.name, "tokens_per_call": wi.B * wi.T, "steps": ri["steps"],
                      "value": si["value"], "unit": "tokens/s", "us_per_call": si["call_us"],
                      "path_roofline_frac": si["path_roofline"]["frac"],
                      "schedule": si["schedule"], "dominant": si["dominant"],
