@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
 
 // The boundary scan for many chains at once: one thread per state element
 // group of 8, walking its chain's chunks in order with the loads of the next
-// W chunks in flight. A wave's load of one chunk covers 1 KB of contiguous
+// W/2 to W chunks in flight. A wave's load of one chunk covers 1 KB of contiguous
 // state (the segmented scan above touches 16 chunks in 64-byte pieces per
 // load and makes two dependent memory round trips per workgroup); with
 // enough chains the loads in flight cover the HBM latency, and each element
@@ -387,30 +387,51 @@ __global__ __launch_bounds__(kThreads) void scan_serial_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) s[c] *= inv;
   }
-  for (int n0 = 0; n0 < N; n0 += W) {
+  // chunk n from slot i (a constant once the loops below are unrolled)
+  auto step = [&](int i, int n) {
+    // the state entering chunk n
+    half8 o;
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-      const int n = n0 + i;
-      if (n < N) {
-        // the state entering chunk n
-        half8 o;
+    for (int c = 0; c < 8; ++c) o[c] = (half_t)s[c];
+    *reinterpret_cast<half8*>(S + n * DKDV) = o;
+    if (row_lead) SS[(long)n * DK] = __builtin_amdgcn_ldexpf(1.f, es);
+    M = a[i].x * M + a[i].y;
+    const int en = row_scale_exp(M);
+    const float f = __builtin_amdgcn_ldexpf(a[i].x, es - en);
+    const float g = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(a[i].y) - en);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = (half_t)s[c];
-        *reinterpret_cast<half8*>(S + n * DKDV) = o;
-        if (row_lead) SS[(long)n * DK] = __builtin_amdgcn_ldexpf(1.f, es);
-        M = a[i].x * M + a[i].y;
-        const int en = row_scale_exp(M);
-        const float f = __builtin_amdgcn_ldexpf(a[i].x, es - en);
-        const float g = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(a[i].y) - en);
+    for (int c = 0; c < 8; ++c) s[c] = fmaf((float)u[i][c], g, f * s[c]);
+    es = en;
+  };
+  // the window as two halves of W/2 chunks: each half is consumed in order
+  // and then refilled at once (chunks W ahead, clamped) while the other
+  // half's loads stay in flight. Whole windows run with no condition inside
+  // and the last N % W chunks after them: with a condition per chunk, or a
+  // slot refilled as soon as it is consumed, the compiler's wait placement
+  // drained the whole window once per W chunks.
+  constexpr int HW = W / 2;
+  auto refill = [&](int h, int nb) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s[c] = fmaf((float)u[i][c], g, f * s[c]);
-        es = en;
-      }
-      const long m = n + W < N ? n + W : N - 1;  // refill the slot (clamped)
-      u[i] = *reinterpret_cast<const half8*>(U + m * DKDV);
-      a[i] = A[m * DK];
+    for (int j = 0; j < HW; ++j) {
+      const long m = nb + j < N ? nb + j : N - 1;
+      u[h * HW + j] = *reinterpret_cast<const half8*>(U + m * DKDV);
+      a[h * HW + j] = A[m * DK];
     }
+  };
+  int n0 = 0;
+  for (; n0 + W <= N; n0 += W) {
+#pragma unroll
+    for (int j = 0; j < HW; ++j) step(j, n0 + j);
+    __builtin_amdgcn_sched_barrier(0);
+    refill(0, n0 + W);
+#pragma unroll
+    for (int j = 0; j < HW; ++j) step(HW + j, n0 + HW + j);
+    __builtin_amdgcn_sched_barrier(0);
+    refill(1, n0 + W + HW);
   }
+#pragma unroll
+  for (int i = 0; i < W - 1; ++i)
+    if (n0 + i < N) step(i, n0 + i);
   if (sfin) {
     const float sc = __builtin_amdgcn_ldexpf(1.f, es);
 #pragma unroll
