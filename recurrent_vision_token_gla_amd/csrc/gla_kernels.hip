@@ -339,45 +339,49 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
 }
 
 // The boundary scan for many chains at once: one thread per state element
-// group of 8, walking its chain's chunks in order with the loads of the next
-// W/2 to W chunks in flight. A wave's load of one chunk covers 1 KB of contiguous
-// state (the segmented scan above touches 16 chunks in 64-byte pieces per
-// load and makes two dependent memory round trips per workgroup); with
+// group of EPT (4 or 8), walking its chain's chunks in order with the loads
+// of the next W/2 to W chunks in flight. A wave's load of one chunk covers
+// 64 EPT contiguous halves of state (the segmented scan above touches 16
+// chunks in 64-byte pieces per load and makes two dependent memory round
+// trips per workgroup); with
 // enough chains the loads in flight cover the HBM latency, and each element
 // follows the recurrence S_{n+1} = a_n S_n + U_n exactly in order. Scales as
-// in scan_kernel; the DV/8 threads of a state row are neighbouring lanes,
+// in scan_kernel; the DV/EPT threads of a state row are neighbouring lanes,
 // which take the row maximum of s0 by lane permutations.
-template <int W>
+template <int W, int EPT>
 __global__ __launch_bounds__(kThreads) void scan_serial_kernel(
     const half_t* __restrict__ Uws, const float* __restrict__ Aws, half_t* __restrict__ Sws,
     float* __restrict__ SigS, const float* s0, float* sfin, int N, int DK, int DV, long groups) {
+  typedef _Float16 HV __attribute__((ext_vector_type(EPT)));
+  typedef float FV __attribute__((ext_vector_type(EPT)));
   const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
-  // groups is a multiple of DV/8, so the lanes of one state row leave together
+  // groups is a multiple of DV/EPT, so the lanes of one state row leave together
   if (gid >= groups) return;
-  const long DKDV = (long)DK * DV, per = DKDV / 8;
+  const long DKDV = (long)DK * DV, per = DKDV / EPT;
   const long bh = gid / per;
-  const int x8 = 8 * (int)(gid - bh * per), d = x8 / DV;
-  const half_t* U = Uws + bh * N * DKDV + x8;
+  const int xg = EPT * (int)(gid - bh * per), d = xg / DV;
+  const half_t* U = Uws + bh * N * DKDV + xg;
   const float2* A = reinterpret_cast<const float2*>(Aws) + bh * N * DK + d;  // (a, m)
-  half_t* S = Sws + bh * N * DKDV + x8;
+  half_t* S = Sws + bh * N * DKDV + xg;
   float* SS = SigS + bh * N * DK + d;
-  const bool row_lead = x8 % DV == 0;
-  float s[8], M = 0.f;
+  const bool row_lead = xg % DV == 0;
+  float s[EPT], M = 0.f;
   if (s0) {
-    load_f8(s0 + bh * DKDV + x8, s);
+    const FV x = *reinterpret_cast<const FV*>(s0 + bh * DKDV + xg);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) M = fmaxf(M, fabsf(s[c]));
-    M = DV == 64 ? group_max<8>(M) : group_max<4>(M);
+    for (int c = 0; c < EPT; ++c) s[c] = x[c], M = fmaxf(M, fabsf(s[c]));
+    if constexpr (EPT == 8) M = DV == 64 ? group_max<8>(M) : group_max<4>(M);
+    else M = DV == 64 ? group_max<16>(M) : group_max<8>(M);
   } else {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[c] = 0.f;
+    for (int c = 0; c < EPT; ++c) s[c] = 0.f;
   }
-  half8 u[W];
+  HV u[W];
   float2 a[W];
 #pragma unroll
   for (int i = 0; i < W; ++i) {
     const long m = i < N ? i : N - 1;
-    u[i] = *reinterpret_cast<const half8*>(U + m * DKDV);
+    u[i] = *reinterpret_cast<const HV*>(U + m * DKDV);
     a[i] = A[m * DK];
   }
   // the state is kept divided by its current row scale 2^es (as in scan_kernel)
@@ -385,22 +389,22 @@ __global__ __launch_bounds__(kThreads) void scan_serial_kernel(
   {
     const float inv = __builtin_amdgcn_ldexpf(1.f, -es);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[c] *= inv;
+    for (int c = 0; c < EPT; ++c) s[c] *= inv;
   }
   // chunk n from slot i (a constant once the loops below are unrolled)
   auto step = [&](int i, int n) {
     // the state entering chunk n
-    half8 o;
+    HV o;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[c] = (half_t)s[c];
-    *reinterpret_cast<half8*>(S + n * DKDV) = o;
+    for (int c = 0; c < EPT; ++c) o[c] = (half_t)s[c];
+    *reinterpret_cast<HV*>(S + n * DKDV) = o;
     if (row_lead) SS[(long)n * DK] = __builtin_amdgcn_ldexpf(1.f, es);
     M = a[i].x * M + a[i].y;
     const int en = row_scale_exp(M);
     const float f = __builtin_amdgcn_ldexpf(a[i].x, es - en);
     const float g = __builtin_amdgcn_ldexpf(1.f, row_scale_exp(a[i].y) - en);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[c] = fmaf((float)u[i][c], g, f * s[c]);
+    for (int c = 0; c < EPT; ++c) s[c] = fmaf((float)u[i][c], g, f * s[c]);
     es = en;
   };
   // the window as two halves of W/2 chunks: each half is consumed in order
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void scan_serial_kernel(
 #pragma unroll
     for (int j = 0; j < HW; ++j) {
       const long m = nb + j < N ? nb + j : N - 1;
-      u[h * HW + j] = *reinterpret_cast<const half8*>(U + m * DKDV);
+      u[h * HW + j] = *reinterpret_cast<const HV*>(U + m * DKDV);
       a[h * HW + j] = A[m * DK];
     }
   };
@@ -434,9 +438,10 @@ __global__ __launch_bounds__(kThreads) void scan_serial_kernel(
     if (n0 + i < N) step(i, n0 + i);
   if (sfin) {
     const float sc = __builtin_amdgcn_ldexpf(1.f, es);
+    FV f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[c] *= sc;
-    store_f8(sfin + bh * DKDV + x8, s);
+    for (int c = 0; c < EPT; ++c) f[c] = s[c] * sc;
+    *reinterpret_cast<FV*>(sfin + bh * DKDV + xg) = f;
   }
 }
 
@@ -517,14 +522,18 @@ hipError_t launch_scan(const Problem& p, int b0, int nb, char* ws, const float* 
   dim3 grid((unsigned)(dkdv / (8 * (kThreads / kScanSegs))), p.H, nb);
   const long groups = (long)nb * p.H * (dkdv / 8);
   if (groups >= kSerialScanGroups || (groups >= kSerialScanGroups / 2 && p.N >= kSerialScanLongChain)) {
-    auto serial = p.N >= 64 ? scan_serial_kernel<16> : scan_serial_kernel<8>;
-    hipLaunchKernelGGL(serial, dim3((unsigned)((groups + kThreads - 1) / kThreads)), dim3(kThreads),
+    // four state elements per thread: twice the waves of eight, and the
+    // scan's issue, not its loads, is what bounds it
+    constexpr int kEpt = 4;
+    const long threads = groups * (8 / kEpt);
+    auto serial = p.N >= 64 ? scan_serial_kernel<16, kEpt> : scan_serial_kernel<8, kEpt>;
+    hipLaunchKernelGGL(serial, dim3((unsigned)((threads + kThreads - 1) / kThreads)), dim3(kThreads),
                        0, s, reinterpret_cast<const half_t*>(ws + w.off_U) + bhn * dkdv,
                        reinterpret_cast<const float*>(ws + w.off_a) + 2 * bhn * p.dk,
                        reinterpret_cast<half_t*>(ws + w.off_S) + bhn * dkdv,
                        reinterpret_cast<float*>(ws + w.off_ss) + bhn * p.dk,
                        s0 ? s0 + st : nullptr, sfin ? sfin + st : nullptr, p.N, p.dk, p.dv,
-                       groups);
+                       threads);
     return hipGetLastError();
   }
   auto kernel = L <= 2 ? scan_kernel<2> : L <= 4 ? scan_kernel<4> : scan_kernel<8>;
