@@ -191,14 +191,13 @@ __global__ __launch_bounds__(kThreads, 7) void summary_kernel(
 constexpr int kScanSegs = 16;  // segments per chain: the lanes of a DPP row
 // The serial scan below replaces the segmented one from this many state
 // element groups of 8 per launch (B H dk dv / 8), or from half as many for
-// chains of 256 chunks and more. Measured on MI355X (64/64, graph-replayed):
-//   groups   N=25            N=100            N=256     (segmented / serial, us)
-//    8,192   3.6 / 4.9       7.7 / 12.2
-//   16,384   4.8 / 5.3      13.1 / 14.6      38.3 / 30.5
-//   32,768   7.4 / 5.9      22.3 / 16.8
-// (serial figures from before its window was refilled in halves and its
-// threads took four elements: about 10% faster since at 32,768 groups and
-// 100 chunks, so the crossover may now lie lower)
+// chains of 256 chunks and more. Measured on MI355X (64/64, each scan alone,
+// 20 launches captured in one graph, segmented / serial, us; the serial scan
+// with its window refilled in halves and four elements per thread):
+//   groups   N=25          N=100          N=256
+//    8,192   4.3 / 5.6     9.2 / 15.7     26.2 / 33.5
+//   16,384   5.7 / 6.0    15.0 / 16.4      - / 33.6 (segmented 38.3 earlier)
+//   32,768    - / 6.6       - / 17.9     (segmented 7.4 and 22.3 earlier)
 constexpr long kSerialScanGroups = 32768;
 constexpr int kSerialScanLongChain = 256;
 
